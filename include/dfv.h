@@ -1,0 +1,166 @@
+/*
+ * dfv.h -- C ABI of the MI355X (gfx950) DFlash2 verification-attention library.
+ *
+ * What the library computes (restated from three pull-request pages of a vLLM
+ * fork; cited by PR number and section):
+ *   [#556] "[Perf] Add opt-in DFlash2 schedules and numerical audits"
+ *   [#587] "[Perf] Reduce DFlash2 long-context verification decay"
+ *   [#589] "[Perf] Reduce DFlash2 attention cost and screen exact QK reuse"
+ *
+ * q draft-verification query tokens (q8 in the pages; 1..8 here), causal among
+ * themselves and placed at the last q positions of the context, with six FP16
+ * query heads sharing one KV head of dimension 256, attend over a paged KV cache
+ * held in OCP E4M3 with per-tensor FP32 scales ([#589] Test Plan; [#556] Test
+ * Plan).  The context is cut into logical splits (80 in the pages: [#587]
+ * Implementation, [#589] Purpose); every split keeps an FP32 online-softmax
+ * state -- running max, compensated sum, FP32 numerator -- and a combine kernel
+ * merges the splits into the FP16 output ([#589] Test Result).  The full FP32
+ * per-split workspace is an output in its own right ([#589] Test Plan).
+ *
+ * Definitions used throughout:
+ *   L_b       context length of sequence b, including its q query tokens.
+ *   p_i       = L_b - q + i, position of query token i; it sees keys 0..p_i.
+ *   row r     = i * 6 + h for query token i and head h (6q rows per sequence).
+ *   S         split size in tokens: desc.split_tokens, or when that is 0 the
+ *             per-sequence rule S = 32 * ceil(ceil(L_b / NS) / 32), which gives
+ *             the pages' 3296-token split at the 261888-token capacity boundary
+ *             ([#589] Test Plan, [#587] Purpose).  Split j covers keys
+ *             [j*S, min((j+1)*S, p_i + 1)) of row (b, i, h).
+ *   c         = softmax_scale * k_scale; score s_t = c * <Q_row, K_t>, where K_t
+ *             and V_t are the E4M3-decoded cache rows of token t.
+ *   state     of split j: m = max_t s_t (natural-log units of the scaled
+ *             score), l = sum_t exp(s_t - m), o[d] = v_scale * sum_t
+ *             exp(s_t - m) * V_t[d].  An empty split is (-inf, 0, 0).
+ *   output    = sum_j e^(m_j - M) o_j / sum_j e^(m_j - M) l_j, M = max_j m_j,
+ *             rounded to FP16 (round to nearest even).
+ *
+ * Memory layouts (all row-major, all device memory owned by the caller):
+ *   q            FP16   [B][q][6][256]
+ *   k_cache      uint8  [num_blocks][16][1][256]   E4M3 codes, 16-token pages
+ *   v_cache      uint8  [num_blocks][16][1][256]
+ *   block_table  int32  [B][max_blocks_per_seq]    token t of sequence b lives in
+ *                                                  page block_table[b][t/16], slot t%16
+ *   context_lens int32  [B]
+ *   k_scale      float32[1], v_scale float32[1]    device scalars (per layer)
+ *   ws_max       float32[B][q][6][NS]
+ *   ws_sum       float32[B][q][6][NS]
+ *   ws_num       float32[B][q][6][NS][256]
+ *   out          FP16   [B][q][6][256]
+ *
+ * Conventions:
+ *   - Every call is asynchronous and stream-ordered on `stream` (a hipStream_t;
+ *     NULL is the default stream).  No call synchronizes the host.
+ *   - The library allocates no memory and keeps no state between calls except
+ *     what the caller hands in (the scratch buffer of the split stage).
+ *   - Every argument the host can check is checked before any launch; on error
+ *     nothing is launched and nothing is written.  A launch failure returns
+ *     DFV_ERR_LAUNCH.  No C++ exception crosses this boundary.
+ *   - Device-resident values cannot be checked without a synchronization.  The
+ *     caller guarantees q <= context_lens[b] <= max_context_len, block ids
+ *     within the caches for every page a context touches, and scales > 0.
+ *     Kernels clamp context_lens[b] into [q, max_context_len], so a bad length
+ *     cannot index past a block-table row.
+ *   - Results are deterministic: the same inputs on the same device give
+ *     byte-identical outputs and workspaces.
+ */
+#ifndef DFV_H_
+#define DFV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define DFV_API __attribute__((visibility("default")))
+#else
+#define DFV_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DFV_OK = 0,
+  DFV_ERR_NULL = -1,        /* a required pointer is NULL                         */
+  DFV_ERR_UNSUPPORTED = -2, /* shape outside the admitted set (caller keeps its own
+                               operator, as the pages' shape-guarded admission does:
+                               [#556] Purpose, [#587] Implementation)              */
+  DFV_ERR_ALIGN = -3,       /* a pointer is not aligned as documented              */
+  DFV_ERR_ARG = -4,         /* an inconsistent size or count                       */
+  DFV_ERR_LAUNCH = -5,      /* the HIP runtime rejected a launch                   */
+  DFV_ERR_DEVICE = -6,      /* no usable gfx950 device for an automatic grid       */
+  DFV_ERR_SCRATCH = -7      /* scratch buffer smaller than dfv_attn_scratch_bytes  */
+} dfv_status;
+
+/* Shape descriptor.  Admitted set: num_q_heads = 6, num_kv_heads = 1,
+ * head_dim = 256, block_size = 16, 1 <= num_q <= 8, 1 <= num_splits <= 256,
+ * batch >= 1, split_tokens = 0 or a positive multiple of 32 with
+ * num_splits * split_tokens >= max_context_len, num_q <= max_context_len <=
+ * 16 * max_blocks_per_seq, softmax_scale > 0 and finite. */
+typedef struct {
+  int32_t batch;              /* B                                                   */
+  int32_t num_q;              /* q, verification tokens per sequence                 */
+  int32_t num_q_heads;        /* 6                                                   */
+  int32_t num_kv_heads;       /* 1                                                   */
+  int32_t head_dim;           /* 256                                                 */
+  int32_t block_size;         /* 16 tokens per page                                  */
+  int32_t max_blocks_per_seq; /* block-table row stride (entries)                    */
+  int32_t num_splits;         /* NS, logical splits (80 in the pages)                */
+  int32_t split_tokens;       /* 0 = per-sequence rule; else fixed S, multiple of 32 */
+  int32_t max_context_len;    /* host-known bound on every context_lens[b]           */
+  int32_t num_workgroups;     /* 0 = one per compute unit of the current device;
+                                 else that many (fixes the scratch size)            */
+  float softmax_scale;        /* 1/sqrt(256) in the pages' configuration             */
+} dfv_attn_desc;
+
+/* Human-readable name of a status code (static string, never NULL). */
+DFV_API const char* dfv_status_string(int status);
+
+/* Validate a descriptor without touching a device.  Returns DFV_OK or the
+ * status any entry point would return for it. */
+DFV_API dfv_status dfv_attn_check(const dfv_attn_desc* desc);
+
+/* Bytes of scratch that dfv_attn_split and dfv_attn need for `desc`: per-split
+ * arrival counters plus partial states of workgroups that share a split.
+ * Returns 0 if the descriptor is invalid or (num_workgroups == 0) no device is
+ * usable.  The scratch must be zero-filled once when allocated; every completed
+ * call leaves its counters at zero again, so one buffer serves any number of
+ * calls (and graph replays) with the same descriptor.  Calls that overlap in
+ * time must not share a scratch buffer. */
+DFV_API size_t dfv_attn_scratch_bytes(const dfv_attn_desc* desc);
+
+/* Split stage: per-split FP32 states of every row ([#587] Implementation:
+ * 80 logical splits, 32-key online updates, compensated FP32 sums, probability
+ * residual products, FP32 state; [#589] Test Plan: full numerator/max/sum
+ * workspace).  Reads q, the caches through block_table, context_lens and the
+ * two scales; writes ws_max, ws_sum, ws_num (every split of every row,
+ * including empty ones) and uses `scratch`.
+ * Alignment: q, k_cache, v_cache, ws_num 16 bytes; others 4 bytes. */
+DFV_API dfv_status dfv_attn_split(const dfv_attn_desc* desc, const void* q,
+                          const uint8_t* k_cache, const uint8_t* v_cache,
+                          const int32_t* block_table, const int32_t* context_lens,
+                          const float* k_scale, const float* v_scale,
+                          float* ws_max, float* ws_sum, float* ws_num,
+                          void* scratch, size_t scratch_bytes, void* stream);
+
+/* Combine stage: merges the NS split states of every row into the FP16 output
+ * ([#589] Test Result: one combine kernel follows each q8 attention kernel).
+ * Reads only the workspace, so it can run on a saved workspace.
+ * Alignment: ws_num and out 16 bytes; others 4 bytes. */
+DFV_API dfv_status dfv_attn_combine(const dfv_attn_desc* desc, const float* ws_max,
+                            const float* ws_sum, const float* ws_num, void* out,
+                            void* stream);
+
+/* Both stages on one stream: dfv_attn_split followed by dfv_attn_combine.
+ * Same arguments, same outputs (workspace and FP16 out). */
+DFV_API dfv_status dfv_attn(const dfv_attn_desc* desc, const void* q, const uint8_t* k_cache,
+                    const uint8_t* v_cache, const int32_t* block_table,
+                    const int32_t* context_lens, const float* k_scale, const float* v_scale,
+                    float* ws_max, float* ws_sum, float* ws_num, void* scratch,
+                    size_t scratch_bytes, void* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DFV_H_ */

@@ -1,0 +1,104 @@
+"""The C-ABI library loads, exports every declared entry point, and rejects bad
+arguments on the host (CPU only: no call here reaches a kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from long_context_split_amd import dfv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dfv.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"DFV_API\s+[\w\s\*]*?\b(dfv_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(dfv.LIB_PATH):
+        pytest.fail("libdfv.so is not built (run long_context_split_amd.build)")
+    return dfv.lib()
+
+
+def test_header_declares_the_documented_entry_points():
+    assert _declared() == sorted(dfv.ENTRY_POINTS)
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in _declared():
+        assert hasattr(L, name), name
+
+
+def test_status_strings(L):
+    for code in range(-7, 1):
+        assert L.dfv_status_string(code).decode().startswith("DFV_")
+    assert b"unknown" in L.dfv_status_string(42)
+
+
+def _good(**kw):
+    base = dict(batch=1, num_q=8, max_blocks=16368, max_context_len=261888, num_workgroups=256)
+    base.update(kw)
+    return dfv.make_desc(base.pop("batch"), base.pop("num_q"), base.pop("max_blocks"),
+                         base.pop("max_context_len"), **base)
+
+
+def test_valid_descriptor(L):
+    assert dfv.check(_good()) == 0
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("num_q_heads", 8, -2), ("num_kv_heads", 2, -2), ("head_dim", 128, -2), ("block_size", 32, -2),
+    ("num_q", 0, -2), ("num_q", 9, -2), ("num_splits", 0, -2), ("num_splits", 257, -2),
+    ("batch", 0, -4), ("max_blocks_per_seq", 0, -4), ("max_context_len", 7, -4),
+    ("max_context_len", 16 * 16368 + 1, -4), ("split_tokens", 48, -4), ("split_tokens", -32, -4),
+    ("split_tokens", 32, -4), ("num_workgroups", -1, -4), ("softmax_scale", 0.0, -4),
+    ("softmax_scale", float("inf"), -4), ("softmax_scale", float("nan"), -4),
+])
+def test_descriptor_admission(L, field, value, status):
+    d = _good()
+    setattr(d, field, value)
+    assert dfv.check(d) == status
+
+
+def test_fixed_split_must_cover_context(L):
+    assert dfv.check(_good(split_tokens=3296)) == 0          # 80 * 3296 >= 261888
+    assert dfv.check(_good(split_tokens=3264)) == -4         # 80 * 3264 <  261888
+
+
+def test_scratch_size_formula(L):
+    d = _good()
+    # counters (80 ints = 320 B, rounded up to 512 B) + (256 + 80) slots of (48*256 + 96) floats
+    assert dfv.scratch_bytes(d) == 512 + (256 + 80) * (48 * 256 + 96) * 4
+    d.num_q_heads = 4
+    assert dfv.scratch_bytes(d) == 0
+
+
+def test_null_and_misaligned_pointers_are_refused_before_launch(L):
+    d = _good()
+    P = ctypes.c_void_p
+    ok = [P(4096 * (i + 1)) for i in range(10)]
+    # null scratch
+    st = L.dfv_attn_split(ctypes.byref(d), *ok, None, 1 << 30, None)
+    assert st == -1
+    # misaligned q
+    args = list(ok)
+    args[0] = P(4096 + 2)
+    st = L.dfv_attn_split(ctypes.byref(d), *args, P(1 << 20), 1 << 30, None)
+    assert st == -3
+    # combine: null out, misaligned numerator
+    assert L.dfv_attn_combine(ctypes.byref(d), P(256), P(512), P(1024), None, None) == -1
+    assert L.dfv_attn_combine(ctypes.byref(d), P(256), P(512), P(1028), P(2048), None) == -3
+    # fused call: bad descriptor first
+    bad = _good(num_q=9)
+    assert L.dfv_attn(ctypes.byref(bad), *ok, P(1 << 20), 1 << 30, P(8192), None) == -2
+
+
+def test_binding_raises_when_library_missing(monkeypatch, tmp_path):
+    monkeypatch.setattr(dfv, "_LIB", None)
+    monkeypatch.setattr(dfv, "LIB_PATH", str(tmp_path / "libdfv.so"))
+    with pytest.raises(FileNotFoundError):
+        dfv.lib()

@@ -1,0 +1,241 @@
+"""HIP path vs the FP64 oracle, element by element, through the C ABI (GPU only).
+
+Inputs come from the seeded synthetic generator; the oracle receives host copies
+of the very same arrays.  Sizes are small enough for the oracle to finish in
+seconds while spanning many 32-key tiles, several workgroups per split and a
+ragged tail; the full-size checks at the end sample outputs the oracle can
+compute one at a time.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from long_context_split_amd import dfv, synth
+from oracle import attention as A
+from tests.parity_util import check_all, check_out, check_ws, oracle_all
+
+pytestmark = pytest.mark.gpu
+
+
+def _note(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def _run(inp, num_splits=80, split_tokens=0, num_workgroups=0, entry="attn"):
+    desc = dfv.desc_for(inp, num_splits=num_splits, split_tokens=split_tokens, num_workgroups=num_workgroups)
+    ws = dfv.Workspace.allocate(desc)
+    if entry == "attn":
+        dfv.run_layer(inp, ws, desc)
+    else:
+        dfv.attn_split(desc, inp.q, inp.k_cache, inp.v_cache, inp.block_table, inp.context_lens,
+                       inp.k_scale, inp.v_scale, ws.ws_max, ws.ws_sum, ws.ws_num, ws.scratch)
+        dfv.attn_combine(desc, ws.ws_max, ws.ws_sum, ws.ws_num, ws.out)
+    torch.cuda.synchronize()
+    res = dict(out=ws.out.float().cpu().numpy(), ws_max=ws.ws_max.cpu().numpy(),
+               ws_sum=ws.ws_sum.cpu().numpy(), ws_num=ws.ws_num.cpu().numpy())
+    return res, ws, desc
+
+
+def _layer(lens, nq, seed, **kw):
+    return synth.make_layer(lens, nq, seed_base=seed, device="cuda", **kw)
+
+
+def test_tiny_workload_full_parity():
+    inp = synth.workload_layer("tiny_ctx4096", 0, device="cuda")
+    _note("tiny_ctx4096 q8 L=4096")
+    res, _, _ = _run(inp)
+    check_all(res, inp.numpy())
+
+
+def test_split_then_combine_entry_points_match_fused_call():
+    inp = synth.workload_layer("tiny_ctx4096", 0, device="cuda")
+    _note("split+combine vs attn")
+    r1, _, _ = _run(inp, entry="attn")
+    r2, _, _ = _run(inp, entry="split")
+    for k in r1:
+        assert np.array_equal(r1[k], r2[k], equal_nan=True), k
+
+
+@pytest.mark.parametrize("L", [8, 9, 15, 16, 17, 31, 32, 33, 63, 64, 65, 100, 257, 1000, 2561, 2592, 2593])
+@pytest.mark.parametrize("nq", [1, 3, 8])
+def test_tail_contexts(L, nq):
+    if L < nq:
+        pytest.skip("context shorter than the query window")
+    _note(f"tail L={L} q={nq}")
+    inp = _layer([L], nq, seed=1000 + L * 10 + nq)
+    res, _, _ = _run(inp)
+    check_all(res, inp.numpy())
+
+
+@pytest.mark.parametrize("nq", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_q_sweep(nq):
+    _note(f"q sweep q={nq} L=3001")
+    inp = _layer([3001], nq, seed=2000 + nq)
+    res, _, _ = _run(inp)
+    check_all(res, inp.numpy())
+
+
+@pytest.mark.parametrize("ns,S", [(1, 0), (7, 0), (80, 0), (256, 0), (80, 64), (2, 3296), (80, 3296), (130, 32)])
+def test_split_variants(ns, S):
+    L = 4160
+    if S and ns * S < L:
+        pytest.skip("splits do not cover the context")
+    _note(f"splits ns={ns} S={S} L={L}")
+    inp = _layer([L], 8, seed=3000 + ns)
+    res, _, _ = _run(inp, num_splits=ns, split_tokens=S)
+    check_all(res, inp.numpy(), num_splits=ns, split_tokens=S)
+
+
+@pytest.mark.parametrize("G", [1, 2, 5, 64, 300, 1024])
+def test_grid_sizes(G):
+    _note(f"grid G={G}")
+    inp = _layer([4096], 8, seed=4000)
+    res, _, _ = _run(inp, num_workgroups=G)
+    check_all(res, inp.numpy())
+
+
+def test_batch_mixed_lengths():
+    _note("batch lens [70, 4096, 1000, 8] q=5")
+    inp = _layer([70, 4096, 1000, 8], 5, seed=5000, max_blocks=300)
+    res, _, _ = _run(inp)
+    check_all(res, inp.numpy())
+
+
+def test_peaky_keys():
+    _note("peaky keys L=20000")
+    inp = _layer([20000], 8, seed=6000, key_mix=0.05)
+    res, _, _ = _run(inp)
+    check_all(res, inp.numpy())
+
+
+@pytest.mark.parametrize("G", [0, 1])
+def test_late_dominant_key_forces_reference_restart(G):
+    # A key far into a wave's range whose score exceeds everything before it by
+    # ~900 natural-log units (> 2^64 in probability) exercises the restart path
+    # (with one workgroup every wave has many tiles before the key).
+    _note(f"late dominant key G={G}")
+    inp = _layer([6000], 4, seed=7000, scales=(0.125, 0.125))
+    inp.q.fill_(1.0)
+    star = 5000
+    bt = inp.block_table.cpu()
+    page = int(bt[0, star // 16])
+    inp.k_cache[page, star % 16, 0, :] = 0x7E          # 448 in every dimension
+    res, _, _ = _run(inp, num_workgroups=G)
+    check_all(res, inp.numpy())
+    d = inp.numpy()
+    v_star = d["v_scale"] * A.e4m3.decode(d["v_cache"][page, star % 16, 0, :])
+    assert np.allclose(res["out"][0, -1, 0], v_star, rtol=2e-3, atol=2e-3)
+
+
+def test_deterministic_and_paging_invariant():
+    _note("determinism + paging")
+    inp = _layer([5000], 8, seed=8000)
+    r1, _, _ = _run(inp)
+    r2, _, _ = _run(inp)
+    for k in r1:
+        assert np.array_equal(r1[k], r2[k]), k
+    # move every physical page to a new place and rewrite the block table
+    nb = inp.k_cache.shape[0]
+    perm = torch.randperm(nb, generator=torch.Generator().manual_seed(1)).cuda()
+    k2 = torch.empty_like(inp.k_cache)
+    v2 = torch.empty_like(inp.v_cache)
+    k2[perm] = inp.k_cache
+    v2[perm] = inp.v_cache
+    inp2 = synth.LayerInputs(inp.q, k2, v2, perm[inp.block_table.long()].to(torch.int32), inp.context_lens,
+                             inp.k_scale, inp.v_scale, inp.softmax_scale)
+    r3, _, _ = _run(inp2)
+    for k in r1:
+        assert np.array_equal(r1[k], r3[k]), k
+
+
+def test_outputs_stay_inside_their_buffers():
+    _note("canaries")
+    inp = _layer([3000], 7, seed=9000)
+    desc = dfv.desc_for(inp)
+    ws = dfv.Workspace.allocate(desc)
+    pad = 4096
+
+    def guarded(t):
+        raw = torch.full((t.numel() * t.element_size() + 2 * pad,), 0xA5, dtype=torch.uint8, device="cuda")
+        inner = raw[pad:pad + t.numel() * t.element_size()].view(t.dtype).view(t.shape)
+        return raw, inner
+
+    outs = {k: guarded(getattr(ws, k)) for k in ("ws_max", "ws_sum", "ws_num", "out")}
+    dfv.attn(desc, inp.q, inp.k_cache, inp.v_cache, inp.block_table, inp.context_lens, inp.k_scale,
+             inp.v_scale, outs["ws_max"][1], outs["ws_sum"][1], outs["ws_num"][1], ws.scratch, outs["out"][1])
+    torch.cuda.synchronize()
+    for k, (raw, inner) in outs.items():
+        r = raw.cpu().numpy()
+        assert np.all(r[:pad] == 0xA5) and np.all(r[-pad:] == 0xA5), k
+    res = dict(out=outs["out"][1].float().cpu().numpy(), ws_max=outs["ws_max"][1].cpu().numpy(),
+               ws_sum=outs["ws_sum"][1].cpu().numpy(), ws_num=outs["ws_num"][1].cpu().numpy())
+    check_all(res, inp.numpy())
+
+
+def test_combine_runs_from_an_oracle_workspace():
+    _note("combine from oracle workspace")
+    inp = _layer([2500], 8, seed=9100)
+    d = inp.numpy()
+    out, m, l, o = oracle_all(d)
+    desc = dfv.desc_for(inp)
+    ws_m = torch.tensor(m, dtype=torch.float32, device="cuda")
+    ws_l = torch.tensor(l, dtype=torch.float32, device="cuda")
+    ws_o = torch.tensor(o, dtype=torch.float32, device="cuda").contiguous()
+    res = torch.empty(1, 8, 6, 256, dtype=torch.float16, device="cuda")
+    dfv.attn_combine(desc, ws_m, ws_l, ws_o, res)
+    torch.cuda.synchronize()
+    check_out(res.float().cpu().numpy(), A.combine(m, l, o))
+
+
+def test_scratch_counters_return_to_zero_and_scratch_is_reusable():
+    _note("scratch reuse")
+    inp = _layer([9000], 8, seed=9200)
+    desc = dfv.desc_for(inp)
+    ws = dfv.Workspace.allocate(desc)
+    for _ in range(3):
+        dfv.run_layer(inp, ws, desc)
+    torch.cuda.synchronize()
+    ncount = desc.batch * desc.num_splits
+    assert int(ws.scratch[: 4 * ncount].view(torch.int32).abs().sum().item()) == 0
+    res = dict(out=ws.out.float().cpu().numpy(), ws_max=ws.ws_max.cpu().numpy(),
+               ws_sum=ws.ws_sum.cpu().numpy(), ws_num=ws.ws_num.cpu().numpy())
+    check_all(res, inp.numpy())
+
+
+def test_too_small_scratch_is_refused_without_launch():
+    inp = _layer([100], 8, seed=9300)
+    desc = dfv.desc_for(inp)
+    ws = dfv.Workspace.allocate(desc)
+    small = ws.scratch[:64]
+    ws.out.fill_(7.0)
+    with pytest.raises(dfv.DfvError) as e:
+        dfv.attn(desc, inp.q, inp.k_cache, inp.v_cache, inp.block_table, inp.context_lens, inp.k_scale,
+                 inp.v_scale, ws.ws_max, ws.ws_sum, ws.ws_num, small, ws.out)
+    assert e.value.status == -7
+    torch.cuda.synchronize()
+    assert bool((ws.out == 7.0).all())
+
+
+# ------------------------------------------------------------------ full sizes, sampled
+
+@pytest.mark.parametrize("name,layer", [("ctx32768_16layer", 3), ("ctx131072_peaky_16layer", 11),
+                                        ("ctx261888_16layer", 0), ("ctx261888_16layer", 15)])
+def test_full_size_sampled(name, layer):
+    _note(f"full size {name} layer {layer}")
+    inp = synth.workload_layer(name, layer, device="cuda")
+    res, _, _ = _run(inp)
+    d = inp.numpy()
+    a = (d["q"], d["k_cache"], d["v_cache"], d["block_table"], d["context_lens"], d["k_scale"],
+         d["v_scale"], d["softmax_scale"])
+    rows = [(0, 0), (3, 4), (7, 5)]
+    ref = A.reference_rows_at(*a, b=0, rows=rows)
+    for k, (i, h) in enumerate(rows):
+        check_out(res["out"][0, i, h][None], ref[k][None])
+    for (i, h, j) in [(0, 0, 0), (7, 5, 79), (4, 2, 40), (7, 0, 78), (1, 3, 13)]:
+        mj, lj, oj = A.split_state_at(*a, b=0, i=i, h=h, j=j)
+        check_ws(res["ws_max"][0, i, h, j][None], res["ws_sum"][0, i, h, j][None],
+                 res["ws_num"][0, i, h, j][None], np.array([mj]), np.array([lj]), oj[None])
+    assert np.all(np.isfinite(res["out"]))
