@@ -50,8 +50,7 @@
  * Conventions:
  *   - Every call is asynchronous and stream-ordered on `stream` (a hipStream_t;
  *     NULL is the default stream).  No call synchronizes the host.
- *   - The library allocates no memory and keeps no state between calls except
- *     what the caller hands in (the scratch buffer of the split stage).
+ *   - The library allocates no memory and keeps no state between calls.
  *   - Every argument the host can check is checked before any launch; on error
  *     nothing is launched and nothing is written.  A launch failure returns
  *     DFV_ERR_LAUNCH.  No C++ exception crosses this boundary.
@@ -88,15 +87,15 @@ typedef enum {
   DFV_ERR_ALIGN = -3,       /* a pointer is not aligned as documented              */
   DFV_ERR_ARG = -4,         /* an inconsistent size or count                       */
   DFV_ERR_LAUNCH = -5,      /* the HIP runtime rejected a launch                   */
-  DFV_ERR_DEVICE = -6,      /* no usable gfx950 device for an automatic grid       */
   DFV_ERR_SCRATCH = -7      /* scratch buffer smaller than dfv_attn_scratch_bytes  */
 } dfv_status;
 
 /* Shape descriptor.  Admitted set: num_q_heads = 6, num_kv_heads = 1,
  * head_dim = 256, block_size = 16, 1 <= num_q <= 8, 1 <= num_splits <= 256,
- * batch >= 1, split_tokens = 0 or a positive multiple of 32 with
- * num_splits * split_tokens >= max_context_len, num_q <= max_context_len <=
- * 16 * max_blocks_per_seq, softmax_scale > 0 and finite. */
+ * batch >= 1, batch * num_splits <= 2^20, split_tokens = 0 or a positive
+ * multiple of 32 with num_splits * split_tokens >= max_context_len,
+ * num_q <= max_context_len <= 16 * max_blocks_per_seq, softmax_scale > 0 and
+ * finite. */
 typedef struct {
   int32_t batch;              /* B                                                   */
   int32_t num_q;              /* q, verification tokens per sequence                 */
@@ -108,8 +107,6 @@ typedef struct {
   int32_t num_splits;         /* NS, logical splits (80 in the pages)                */
   int32_t split_tokens;       /* 0 = per-sequence rule; else fixed S, multiple of 32 */
   int32_t max_context_len;    /* host-known bound on every context_lens[b]           */
-  int32_t num_workgroups;     /* 0 = one per compute unit of the current device;
-                                 else that many (fixes the scratch size)            */
   float softmax_scale;        /* 1/sqrt(256) in the pages' configuration             */
 } dfv_attn_desc;
 
@@ -120,21 +117,20 @@ DFV_API const char* dfv_status_string(int status);
  * status any entry point would return for it. */
 DFV_API dfv_status dfv_attn_check(const dfv_attn_desc* desc);
 
-/* Bytes of scratch that dfv_attn_split and dfv_attn need for `desc`: per-split
- * arrival counters plus partial states of workgroups that share a split.
- * Returns 0 if the descriptor is invalid or (num_workgroups == 0) no device is
- * usable.  The scratch must be zero-filled once when allocated; every completed
- * call leaves its counters at zero again, so one buffer serves any number of
- * calls (and graph replays) with the same descriptor.  Calls that overlap in
- * time must not share a scratch buffer. */
-DFV_API size_t dfv_attn_scratch_bytes(const dfv_attn_desc* desc);
+/* Bytes of caller-provided scratch that dfv_attn_split and dfv_attn need for
+ * `desc`, written to *bytes.  With the current kernels it is always 0 (every
+ * split state is produced inside one workgroup), and `scratch` may be NULL;
+ * the argument is kept so that later kernels may use scratch without an ABI
+ * change.  Returns the descriptor's status. */
+DFV_API dfv_status dfv_attn_scratch_bytes(const dfv_attn_desc* desc, size_t* bytes);
 
 /* Split stage: per-split FP32 states of every row ([#587] Implementation:
  * 80 logical splits, 32-key online updates, compensated FP32 sums, probability
  * residual products, FP32 state; [#589] Test Plan: full numerator/max/sum
  * workspace).  Reads q, the caches through block_table, context_lens and the
  * two scales; writes ws_max, ws_sum, ws_num (every split of every row,
- * including empty ones) and uses `scratch`.
+ * including empty ones).  scratch_bytes must be at least what
+ * dfv_attn_scratch_bytes reports (scratch may be NULL when that is 0).
  * Alignment: q, k_cache, v_cache, ws_num 16 bytes; others 4 bytes. */
 DFV_API dfv_status dfv_attn_split(const dfv_attn_desc* desc, const void* q,
                           const uint8_t* k_cache, const uint8_t* v_cache,

@@ -9,74 +9,82 @@
 // empty splits (m_j = -inf) carrying no weight; the result is rounded to FP16
 // with round-to-nearest-even.
 //
-// One workgroup per row, four waves; wave v merges splits j = v, v+4, ... with
-// lane l owning dimensions 4l..4l+3 (16-byte loads of the numerator rows), then
-// the four wave partials are merged in wave order through LDS.  The order of
-// every sum is fixed, so results are byte-deterministic.  The workload is tiny
-// (NS * 1 KB per row), so the kernel is latency-bound; four waves per row keep
-// four independent load streams in flight.
+// The workload is small (NS KB per row) and latency-bound, so it is spread
+// wide: one workgroup per (row, quarter of the 256 dimensions), four waves per
+// workgroup.  Every wave reduces M over all splits itself (no barrier), then
+// wave v accumulates splits j = v, v+4, ... with each lane owning one dimension
+// and all of its loads issued before use; the four partial sums are added in
+// wave order through LDS.  Every sum has a fixed order, so results are
+// byte-deterministic.
 #include "dfv_common.h"
 
 namespace dfv {
 namespace {
 
-typedef float float4v __attribute__((ext_vector_type(4)));
 constexpr float kNegInf = -__builtin_inff();
+constexpr int kChunk = 8;   // loads in flight per lane and batch
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
+  return x;
+}
 
 __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
-  __shared__ float s_m[kWaves];
-  __shared__ float s_l[kWaves];
-  __shared__ __attribute__((aligned(16))) float s_o[kWaves][kHeadDim];
-  const int row = blockIdx.x;
+  __shared__ float s_num[kWaves][64];
+  __shared__ float s_den[kWaves];
+  const int row = blockIdx.x >> 2;
+  const int quarter = blockIdx.x & 3;
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int NS = a.num_splits;
   const float* mrow = a.ws_max + (size_t)row * NS;
   const float* lrow = a.ws_sum + (size_t)row * NS;
-  const float* orow = a.ws_num + (size_t)row * NS * kHeadDim;
+  const float* orow = a.ws_num + (size_t)row * NS * kHeadDim + 64 * quarter + lane;
 
   float M = kNegInf;
-  for (int j = wave; j < NS; j += kWaves) M = fmaxf(M, mrow[j]);
-  float4v acc = {0.f, 0.f, 0.f, 0.f};
-  float l = 0.f;
+  for (int j = lane; j < NS; j += 64) M = fmaxf(M, mrow[j]);
+  M = wave_max(M);
+
+  float num = 0.f, den = 0.f;
   if (M != kNegInf) {
-    for (int j = wave; j < NS; j += kWaves) {
-      const float mj = mrow[j];
-      if (mj == kNegInf) continue;
-      const float e = __expf(mj - M);
-      acc += *(const float4v*)(orow + (size_t)j * kHeadDim + 4 * lane) * e;
-      l += lrow[j] * e;
+    for (int j0 = wave; j0 < NS; j0 += kWaves * kChunk) {
+      float ov[kChunk];
+#pragma unroll
+      for (int k = 0; k < kChunk; ++k) {
+        const int j = j0 + kWaves * k;
+        ov[k] = j < NS ? orow[(size_t)j * kHeadDim] : 0.f;
+      }
+#pragma unroll
+      for (int k = 0; k < kChunk; ++k) {
+        const int j = j0 + kWaves * k;
+        if (j < NS) {
+          const float mj = mrow[j];
+          const float e = (mj == kNegInf) ? 0.f : __expf(mj - M);
+          num += ov[k] * e;
+          den += lrow[j] * e;
+        }
+      }
     }
   }
-  if (lane == 0) {
-    s_m[wave] = M;
-    s_l[wave] = l;
-  }
-  *(float4v*)&s_o[wave][4 * lane] = acc;
+  s_num[wave][lane] = num;
+  if (lane == 0) s_den[wave] = den;
   __syncthreads();
   if (wave == 0) {
-    float Mt = kNegInf;
-#pragma unroll
-    for (int v = 0; v < kWaves; ++v) Mt = fmaxf(Mt, s_m[v]);
-    float4v num = {0.f, 0.f, 0.f, 0.f};
-    float den = 0.f;
+    float n = 0.f, d = 0.f;
 #pragma unroll
     for (int v = 0; v < kWaves; ++v) {
-      if (s_m[v] == kNegInf) continue;
-      const float e = __expf(s_m[v] - Mt);
-      num += *(const float4v*)&s_o[v][4 * lane] * e;
-      den += s_l[v] * e;
+      n += s_num[v][lane];
+      d += s_den[v];
     }
-    _Float16* o = a.out + (size_t)row * kHeadDim + 4 * lane;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) o[k] = (_Float16)(num[k] / den);
+    a.out[(size_t)row * kHeadDim + 64 * quarter + lane] = (_Float16)(n / d);
   }
 }
 
 }  // namespace
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(combine_kernel, dim3(a.rows), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL(combine_kernel, dim3(4 * a.rows), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -24,7 +24,8 @@ dfv_status check_desc(const dfv_attn_desc* d) {
     return DFV_ERR_UNSUPPORTED;
   if (d->num_q < 1 || d->num_q > dfv::kMaxQ) return DFV_ERR_UNSUPPORTED;
   if (d->num_splits < 1 || d->num_splits > dfv::kMaxSplits) return DFV_ERR_UNSUPPORTED;
-  if (d->batch < 1 || d->max_blocks_per_seq < 1 || d->num_workgroups < 0) return DFV_ERR_ARG;
+  if (d->batch < 1 || d->max_blocks_per_seq < 1) return DFV_ERR_ARG;
+  if ((long long)d->batch * d->num_splits > (1LL << 20)) return DFV_ERR_ARG;
   if (d->max_context_len < d->num_q) return DFV_ERR_ARG;
   if ((long long)d->max_context_len > 16LL * d->max_blocks_per_seq) return DFV_ERR_ARG;
   if (d->split_tokens < 0 || d->split_tokens % dfv::kTile != 0) return DFV_ERR_ARG;
@@ -34,25 +35,13 @@ dfv_status check_desc(const dfv_attn_desc* d) {
   return DFV_OK;
 }
 
-// Grid size: the descriptor's, else one workgroup per compute unit of the
-// current device (the kernel holds one 256-thread workgroup per CU).
-dfv_status grid_size(const dfv_attn_desc* d, int* out) {
-  if (d->num_workgroups > 0) {
-    *out = d->num_workgroups;
-    return DFV_OK;
-  }
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return DFV_ERR_DEVICE;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-    return DFV_ERR_DEVICE;
-  *out = cus;
-  return DFV_OK;
-}
+// Scratch the kernels need: none (each split state is built inside one workgroup).
+size_t scratch_need(const dfv_attn_desc*) { return 0; }
 
 dfv_status check_split_ptrs(const void* q, const uint8_t* kc, const uint8_t* vc, const int32_t* bt,
                             const int32_t* cl, const float* ks, const float* vs, const float* wm,
                             const float* wl, const float* wn, const void* scratch) {
-  if (!q || !kc || !vc || !bt || !cl || !ks || !vs || !wm || !wl || !wn || !scratch) return DFV_ERR_NULL;
+  if (!q || !kc || !vc || !bt || !cl || !ks || !vs || !wm || !wl || !wn) return DFV_ERR_NULL;
   if (!aligned(q, 16) || !aligned(kc, 16) || !aligned(vc, 16) || !aligned(wn, 16) || !aligned(bt, 4) ||
       !aligned(cl, 4) || !aligned(ks, 4) || !aligned(vs, 4) || !aligned(wm, 4) || !aligned(wl, 4) ||
       !aligned(scratch, 256))
@@ -70,10 +59,8 @@ dfv_status launch_split_checked(const dfv_attn_desc* d, const void* q, const uin
                                 const uint8_t* vc, const int32_t* bt, const int32_t* cl,
                                 const float* ks, const float* vs, float* wm, float* wl, float* wn,
                                 void* scratch, size_t scratch_bytes, hipStream_t stream) {
-  int G = 0;
-  dfv_status s = grid_size(d, &G);
-  if (s != DFV_OK) return s;
-  if (scratch_bytes < dfv::scratch_bytes(d->batch, d->num_splits, G)) return DFV_ERR_SCRATCH;
+  (void)scratch;
+  if (scratch_bytes < scratch_need(d)) return DFV_ERR_SCRATCH;
   dfv::SplitArgs a;
   a.q = (const _Float16*)q;
   a.k_cache = kc;
@@ -85,8 +72,6 @@ dfv_status launch_split_checked(const dfv_attn_desc* d, const void* q, const uin
   a.ws_max = wm;
   a.ws_sum = wl;
   a.ws_num = wn;
-  a.counters = (int*)scratch;
-  a.partials = (float*)((char*)scratch + dfv::counter_bytes(d->batch, d->num_splits));
   a.batch = d->batch;
   a.num_q = d->num_q;
   a.max_blocks = d->max_blocks_per_seq;
@@ -94,7 +79,7 @@ dfv_status launch_split_checked(const dfv_attn_desc* d, const void* q, const uin
   a.split_tokens = d->split_tokens;
   a.max_context_len = d->max_context_len;
   a.softmax_scale = d->softmax_scale;
-  return dfv::launch_split(a, G, stream) == hipSuccess ? DFV_OK : DFV_ERR_LAUNCH;
+  return dfv::launch_split(a, stream) == hipSuccess ? DFV_OK : DFV_ERR_LAUNCH;
 }
 
 dfv_status launch_combine_checked(const dfv_attn_desc* d, const float* wm, const float* wl,
@@ -121,7 +106,6 @@ const char* dfv_status_string(int status) {
     case DFV_ERR_ALIGN: return "DFV_ERR_ALIGN: pointer misaligned";
     case DFV_ERR_ARG: return "DFV_ERR_ARG: inconsistent size or count";
     case DFV_ERR_LAUNCH: return "DFV_ERR_LAUNCH: kernel launch failed";
-    case DFV_ERR_DEVICE: return "DFV_ERR_DEVICE: no usable device";
     case DFV_ERR_SCRATCH: return "DFV_ERR_SCRATCH: scratch buffer too small";
     default: return "unknown dfv status";
   }
@@ -129,11 +113,12 @@ const char* dfv_status_string(int status) {
 
 dfv_status dfv_attn_check(const dfv_attn_desc* desc) { return check_desc(desc); }
 
-size_t dfv_attn_scratch_bytes(const dfv_attn_desc* desc) {
-  if (check_desc(desc) != DFV_OK) return 0;
-  int G = 0;
-  if (grid_size(desc, &G) != DFV_OK) return 0;
-  return dfv::scratch_bytes(desc->batch, desc->num_splits, G);
+dfv_status dfv_attn_scratch_bytes(const dfv_attn_desc* desc, size_t* bytes) {
+  if (!bytes) return DFV_ERR_NULL;
+  *bytes = 0;
+  const dfv_status s = check_desc(desc);
+  if (s == DFV_OK) *bytes = scratch_need(desc);
+  return s;
 }
 
 dfv_status dfv_attn_split(const dfv_attn_desc* desc, const void* q, const uint8_t* k_cache,
@@ -170,10 +155,7 @@ dfv_status dfv_attn(const dfv_attn_desc* desc, const void* q, const uint8_t* k_c
   if (s != DFV_OK) return s;
   s = check_combine_ptrs(ws_max, ws_sum, ws_num, out);
   if (s != DFV_OK) return s;
-  int G = 0;
-  s = grid_size(desc, &G);
-  if (s != DFV_OK) return s;
-  if (scratch_bytes < dfv::scratch_bytes(desc->batch, desc->num_splits, G)) return DFV_ERR_SCRATCH;
+  if (scratch_bytes < scratch_need(desc)) return DFV_ERR_SCRATCH;
   s = launch_split_checked(desc, q, k_cache, v_cache, block_table, context_lens, k_scale, v_scale,
                            ws_max, ws_sum, ws_num, scratch, scratch_bytes, (hipStream_t)stream);
   if (s != DFV_OK) return s;

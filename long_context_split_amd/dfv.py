@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(PKG, "libdfv.so")
 
 DFV_OK = 0
 STATUS = {0: "DFV_OK", -1: "DFV_ERR_NULL", -2: "DFV_ERR_UNSUPPORTED", -3: "DFV_ERR_ALIGN",
-          -4: "DFV_ERR_ARG", -5: "DFV_ERR_LAUNCH", -6: "DFV_ERR_DEVICE", -7: "DFV_ERR_SCRATCH"}
+          -4: "DFV_ERR_ARG", -5: "DFV_ERR_LAUNCH", -7: "DFV_ERR_SCRATCH"}
 ENTRY_POINTS = ("dfv_status_string", "dfv_attn_check", "dfv_attn_scratch_bytes", "dfv_attn_split",
                 "dfv_attn_combine", "dfv_attn")
 
@@ -32,8 +32,7 @@ class Desc(ctypes.Structure):
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("block_size", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
                 ("num_splits", ctypes.c_int32), ("split_tokens", ctypes.c_int32),
-                ("max_context_len", ctypes.c_int32), ("num_workgroups", ctypes.c_int32),
-                ("softmax_scale", ctypes.c_float)]
+                ("max_context_len", ctypes.c_int32), ("softmax_scale", ctypes.c_float)]
 
 
 _LIB = None
@@ -52,8 +51,8 @@ def lib():
         L.dfv_status_string.restype = ctypes.c_char_p
         L.dfv_attn_check.argtypes = [ctypes.POINTER(Desc)]
         L.dfv_attn_check.restype = ctypes.c_int
-        L.dfv_attn_scratch_bytes.argtypes = [ctypes.POINTER(Desc)]
-        L.dfv_attn_scratch_bytes.restype = ctypes.c_size_t
+        L.dfv_attn_scratch_bytes.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(ctypes.c_size_t)]
+        L.dfv_attn_scratch_bytes.restype = ctypes.c_int
         L.dfv_attn_split.argtypes = [ctypes.POINTER(Desc)] + [_P] * 10 + [_P, ctypes.c_size_t, _P]
         L.dfv_attn_split.restype = ctypes.c_int
         L.dfv_attn_combine.argtypes = [ctypes.POINTER(Desc), _P, _P, _P, _P, _P]
@@ -65,11 +64,10 @@ def lib():
 
 
 def make_desc(batch: int, num_q: int, max_blocks: int, max_context_len: int, *, num_splits: int = 80,
-              split_tokens: int = 0, num_workgroups: int = 0, softmax_scale: float = 1.0 / 16.0,
-              num_q_heads: int = 6, num_kv_heads: int = 1, head_dim: int = 256,
-              block_size: int = 16) -> Desc:
+              split_tokens: int = 0, softmax_scale: float = 1.0 / 16.0, num_q_heads: int = 6,
+              num_kv_heads: int = 1, head_dim: int = 256, block_size: int = 16) -> Desc:
     return Desc(batch, num_q, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks, num_splits,
-                split_tokens, max_context_len, num_workgroups, softmax_scale)
+                split_tokens, max_context_len, softmax_scale)
 
 
 def check(desc: Desc) -> int:
@@ -77,7 +75,9 @@ def check(desc: Desc) -> int:
 
 
 def scratch_bytes(desc: Desc) -> int:
-    return int(lib().dfv_attn_scratch_bytes(ctypes.byref(desc)))
+    n = ctypes.c_size_t(0)
+    _raise(lib().dfv_attn_scratch_bytes(ctypes.byref(desc), ctypes.byref(n)), "dfv_attn_scratch_bytes")
+    return int(n.value)
 
 
 def _ptr(t) -> Optional[int]:
@@ -110,13 +110,11 @@ class Workspace:
         import torch
         rows = (desc.batch, desc.num_q, desc.num_q_heads)
         nbytes = scratch_bytes(desc)
-        if nbytes == 0:
-            raise DfvError(check(desc) or -6, "dfv_attn_scratch_bytes")
         return Workspace(
             ws_max=torch.empty(*rows, desc.num_splits, dtype=torch.float32, device=device),
             ws_sum=torch.empty(*rows, desc.num_splits, dtype=torch.float32, device=device),
             ws_num=torch.empty(*rows, desc.num_splits, desc.head_dim, dtype=torch.float32, device=device),
-            scratch=torch.zeros(nbytes, dtype=torch.uint8, device=device),
+            scratch=torch.zeros(nbytes, dtype=torch.uint8, device=device) if nbytes else None,
             out=torch.empty(*rows, desc.head_dim, dtype=torch.float16, device=device))
 
 
@@ -153,10 +151,10 @@ def run_layer(inp, ws: Workspace, desc: Desc, stream=None):
     return ws
 
 
-def desc_for(inp, *, num_splits: int = 80, split_tokens: int = 0, num_workgroups: int = 0) -> Desc:
+def desc_for(inp, *, num_splits: int = 80, split_tokens: int = 0) -> Desc:
     """Descriptor matching a ``synth.LayerInputs``."""
     B, nq, hq, d = inp.q.shape
     lens = [int(x) for x in inp.context_lens.cpu().tolist()]
     return make_desc(B, nq, inp.block_table.shape[1], max(lens), num_splits=num_splits,
-                     split_tokens=split_tokens, num_workgroups=num_workgroups,
-                     softmax_scale=inp.softmax_scale, num_q_heads=hq, head_dim=d)
+                     split_tokens=split_tokens, softmax_scale=inp.softmax_scale, num_q_heads=hq,
+                     head_dim=d)

@@ -34,13 +34,13 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_status_strings(L):
-    for code in range(-7, 1):
+    for code in (0, -1, -2, -3, -4, -5, -7):
         assert L.dfv_status_string(code).decode().startswith("DFV_")
     assert b"unknown" in L.dfv_status_string(42)
 
 
 def _good(**kw):
-    base = dict(batch=1, num_q=8, max_blocks=16368, max_context_len=261888, num_workgroups=256)
+    base = dict(batch=1, num_q=8, max_blocks=16368, max_context_len=261888)
     base.update(kw)
     return dfv.make_desc(base.pop("batch"), base.pop("num_q"), base.pop("max_blocks"),
                          base.pop("max_context_len"), **base)
@@ -55,7 +55,7 @@ def test_valid_descriptor(L):
     ("num_q", 0, -2), ("num_q", 9, -2), ("num_splits", 0, -2), ("num_splits", 257, -2),
     ("batch", 0, -4), ("max_blocks_per_seq", 0, -4), ("max_context_len", 7, -4),
     ("max_context_len", 16 * 16368 + 1, -4), ("split_tokens", 48, -4), ("split_tokens", -32, -4),
-    ("split_tokens", 32, -4), ("num_workgroups", -1, -4), ("softmax_scale", 0.0, -4),
+    ("split_tokens", 32, -4), ("softmax_scale", 0.0, -4),
     ("softmax_scale", float("inf"), -4), ("softmax_scale", float("nan"), -4),
 ])
 def test_descriptor_admission(L, field, value, status):
@@ -69,21 +69,31 @@ def test_fixed_split_must_cover_context(L):
     assert dfv.check(_good(split_tokens=3264)) == -4         # 80 * 3264 <  261888
 
 
-def test_scratch_size_formula(L):
+def test_scratch_size_is_zero_and_reported_through_out_parameter(L):
     d = _good()
-    # counters (80 ints = 320 B, rounded up to 512 B) + (256 + 80) slots of (48*256 + 96) floats
-    assert dfv.scratch_bytes(d) == 512 + (256 + 80) * (48 * 256 + 96) * 4
-    d.num_q_heads = 4
     assert dfv.scratch_bytes(d) == 0
+    n = ctypes.c_size_t(123)
+    d.num_q_heads = 4
+    assert L.dfv_attn_scratch_bytes(ctypes.byref(d), ctypes.byref(n)) == -2 and n.value == 0
+    assert L.dfv_attn_scratch_bytes(ctypes.byref(_good()), None) == -1
+
+
+def test_batch_times_splits_bound(L):
+    assert dfv.check(_good(batch=4096, num_splits=256)) == 0
+    assert dfv.check(_good(batch=4097, num_splits=256)) == -4
 
 
 def test_null_and_misaligned_pointers_are_refused_before_launch(L):
     d = _good()
     P = ctypes.c_void_p
     ok = [P(4096 * (i + 1)) for i in range(10)]
-    # null scratch
-    st = L.dfv_attn_split(ctypes.byref(d), *ok, None, 1 << 30, None)
+    # a null required pointer (block table)
+    args = list(ok)
+    args[3] = None
+    st = L.dfv_attn_split(ctypes.byref(d), *args, None, 0, None)
     assert st == -1
+    # misaligned scratch
+    assert L.dfv_attn_split(ctypes.byref(d), *ok, P(4096 + 8), 0, None) == -3
     # misaligned q
     args = list(ok)
     args[0] = P(4096 + 2)
