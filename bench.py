@@ -100,6 +100,7 @@ def main():
     L = w["context"]
     desc = dfv.desc_for(layers[0])
     wss = [dfv.Workspace.allocate(desc) for _ in layers]
+    cbufs = [dfv.chunk_buffers(desc) for _ in layers]
     stream = torch.cuda.current_stream()
 
     def step():
@@ -110,6 +111,11 @@ def main():
         for inp, ws in zip(layers, wss):
             dfv.attn_split(desc, inp.q, inp.k_cache, inp.v_cache, inp.block_table, inp.context_lens,
                            inp.k_scale, inp.v_scale, ws.ws_max, ws.ws_sum, ws.ws_num, ws.scratch, stream)
+
+    def split_kernel_only():
+        for inp, cb in zip(layers, cbufs):
+            dfv.attn_split_chunks(desc, inp.q, inp.k_cache, inp.v_cache, inp.block_table,
+                                  inp.context_lens, inp.k_scale, inp.v_scale, *cb, stream)
 
     def combine_only():
         for ws in wss:
@@ -143,7 +149,11 @@ def main():
     total_ms = timed(run, args.steps)
     ms_per_step = total_ms / args.steps
 
-    # dominant kernel alone (split stage), same stream, same layers
+    # dominant kernel alone (the split kernel writing key-chunk states), then the
+    # split stage (split kernel + chunk merge) and the combine, same stream, same layers
+    for _ in range(args.warmup):
+        split_kernel_only()
+    kernel_ms = timed(split_kernel_only, args.steps) / (args.steps * len(layers))
     split_ms = timed(split_only, args.steps) / (args.steps * len(layers))
     combine_ms = timed(combine_only, args.steps) / (args.steps * len(layers))
 
@@ -151,7 +161,7 @@ def main():
     nrows = nq * 6
     ws_bytes = nrows * 80 * (256 + 2) * 4
     all_bytes_layer = kv_bytes_layer + nrows * 256 * 2 + (-(-L // 16)) * 4 + 2 * ws_bytes + nrows * 256 * 2
-    achieved = kv_bytes_layer / (split_ms * 1e-3) / 1e9
+    achieved = kv_bytes_layer / (kernel_ms * 1e-3) / 1e9
     traffic = measured_traffic(kv_bytes_layer)
 
     line = {
@@ -173,7 +183,9 @@ def main():
                    "timing": "hip graph replay" if graph else "stream launches"},
         "kv_GBps_whole_step": round(kv_bytes_layer * len(layers) / (ms_per_step * 1e-3) / 1e9, 1),
         "all_bytes_GBps_whole_step": round(all_bytes_layer * len(layers) / (ms_per_step * 1e-3) / 1e9, 1),
-        "split_ms_per_launch": round(split_ms, 5),
+        "split_kernel_ms_per_launch": round(kernel_ms, 5),
+        "split_stage_ms_per_call": round(split_ms, 5),
+        "key_chunks_per_split": dfv.chunks(desc),
         "combine_ms_per_launch": round(combine_ms, 5),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),

@@ -50,7 +50,8 @@
  * Conventions:
  *   - Every call is asynchronous and stream-ordered on `stream` (a hipStream_t;
  *     NULL is the default stream).  No call synchronizes the host.
- *   - The library allocates no memory and keeps no state between calls.
+ *   - The library allocates no memory and keeps no state between calls except
+ *     what the caller hands in (the scratch buffer of the split stage).
  *   - Every argument the host can check is checked before any launch; on error
  *     nothing is launched and nothing is written.  A launch failure returns
  *     DFV_ERR_LAUNCH.  No C++ exception crosses this boundary.
@@ -118,10 +119,14 @@ DFV_API const char* dfv_status_string(int status);
 DFV_API dfv_status dfv_attn_check(const dfv_attn_desc* desc);
 
 /* Bytes of caller-provided scratch that dfv_attn_split and dfv_attn need for
- * `desc`, written to *bytes.  With the current kernels it is always 0 (every
- * split state is produced inside one workgroup), and `scratch` may be NULL;
- * the argument is kept so that later kernels may use scratch without an ABI
- * change.  Returns the descriptor's status. */
+ * `desc`, written to *bytes.  To fill the GPU every logical split is cut into
+ * C = max(1, min(4, 256 / (batch * num_splits))) key chunks processed by
+ * separate workgroups; with C > 1 their FP32 states (B*q*6*NS*C of them,
+ * 258 floats each) are staged in the scratch buffer and merged, in chunk
+ * order, into the workspace by a second kernel.  With C = 1 the size is 0 and
+ * `scratch` may be NULL.  The contents need no initialisation and are
+ * meaningless between calls.  Calls that may overlap in time must not share a
+ * scratch buffer.  Returns the descriptor's status. */
 DFV_API dfv_status dfv_attn_scratch_bytes(const dfv_attn_desc* desc, size_t* bytes);
 
 /* Split stage: per-split FP32 states of every row ([#587] Implementation:
@@ -131,6 +136,7 @@ DFV_API dfv_status dfv_attn_scratch_bytes(const dfv_attn_desc* desc, size_t* byt
  * two scales; writes ws_max, ws_sum, ws_num (every split of every row,
  * including empty ones).  scratch_bytes must be at least what
  * dfv_attn_scratch_bytes reports (scratch may be NULL when that is 0).
+ * Launches the split kernel and, with C > 1 key chunks, the chunk merge.
  * Alignment: q, k_cache, v_cache, ws_num 16 bytes; others 4 bytes. */
 DFV_API dfv_status dfv_attn_split(const dfv_attn_desc* desc, const void* q,
                           const uint8_t* k_cache, const uint8_t* v_cache,
@@ -138,6 +144,29 @@ DFV_API dfv_status dfv_attn_split(const dfv_attn_desc* desc, const void* q,
                           const float* k_scale, const float* v_scale,
                           float* ws_max, float* ws_sum, float* ws_num,
                           void* scratch, size_t scratch_bytes, void* stream);
+
+/* Number of key chunks C >= 1 each logical split is cut into for `desc`
+ * (C = max(1, min(4, 256 / (batch * num_splits)))), written to *chunks.
+ * Returns the descriptor's status. */
+DFV_API dfv_status dfv_attn_chunks(const dfv_attn_desc* desc, int32_t* chunks);
+
+/* The split stage's first kernel on its own: the FP32 state of every
+ * (row, split j, key chunk c), the same state definition as the workspace
+ * applied to the chunk's keys.  With T = ceil(L_b / 32) key tiles, split j
+ * holds tiles [a_j, b_j) = [min(j*S/32, T), min((j+1)*S/32, T)); with
+ * n_j = b_j - a_j, chunk c holds tiles [a_j + floor(c*n_j/C), a_j +
+ * floor((c+1)*n_j/C)), i.e. keys 32x that, cut at the row's causal bound p_i.
+ * Layout: chunk_max, chunk_sum float32[B][q][6][NS][C], chunk_num
+ * float32[B][q][6][NS][C][256] (the workspace layout when C = 1, so the
+ * workspace buffers may be passed).  dfv_attn_split is this kernel followed,
+ * when C > 1, by a merge of the C chunk states of each split in chunk order.
+ * Alignment: q, k_cache, v_cache, chunk_num 16 bytes; others 4 bytes. */
+DFV_API dfv_status dfv_attn_split_chunks(const dfv_attn_desc* desc, const void* q,
+                                 const uint8_t* k_cache, const uint8_t* v_cache,
+                                 const int32_t* block_table, const int32_t* context_lens,
+                                 const float* k_scale, const float* v_scale,
+                                 float* chunk_max, float* chunk_sum, float* chunk_num,
+                                 void* stream);
 
 /* Combine stage: merges the NS split states of every row into the FP16 output
  * ([#589] Test Result: one combine kernel follows each q8 attention kernel).
@@ -147,8 +176,9 @@ DFV_API dfv_status dfv_attn_combine(const dfv_attn_desc* desc, const float* ws_m
                             const float* ws_sum, const float* ws_num, void* out,
                             void* stream);
 
-/* Both stages on one stream: dfv_attn_split followed by dfv_attn_combine.
- * Same arguments, same outputs (workspace and FP16 out). */
+/* Both stages on one stream: the results (workspace and FP16 out) are
+ * byte-identical to dfv_attn_split followed by dfv_attn_combine; with C > 1
+ * the chunk merge and the combine run as one kernel. */
 DFV_API dfv_status dfv_attn(const dfv_attn_desc* desc, const void* q, const uint8_t* k_cache,
                     const uint8_t* v_cache, const int32_t* block_table,
                     const int32_t* context_lens, const float* k_scale, const float* v_scale,

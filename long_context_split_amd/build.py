@@ -26,6 +26,9 @@ HIPCC_FLAGS = [
     "-fvisibility=hidden",
     # packed FP32 instructions stay off: the compiler's own plain float code only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in VGPRs: the split kernel's O tiles otherwise bounce
+    # between VGPRs and AGPRs every key tile
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wno-unused-command-line-argument",
 ]
 

@@ -1,4 +1,5 @@
-// Combine stage of DFlash2 verification attention on gfx950 (MI355X).
+// Combine stage of DFlash2 verification attention on gfx950 (MI355X), and the
+// merge of key-chunk states into the per-split workspace.
 //
 // Page cited: [#589] "[Perf] Reduce DFlash2 attention cost and screen exact QK
 // reuse", Test Result (each q8 attention kernel is followed by a combine kernel
@@ -7,22 +8,26 @@
 // For one query row the NS split states (m_j, l_j, o_j) merge by log-sum-exp:
 //   M = max_j m_j,  out = sum_j e^(m_j - M) o_j / sum_j e^(m_j - M) l_j,
 // empty splits (m_j = -inf) carrying no weight; the result is rounded to FP16
-// with round-to-nearest-even.
+// with round-to-nearest-even.  When the split kernel cut every split into C key
+// chunks, the chunk states of split j merge the same way first,
+//   m_j = max_c m_jc,  l_j = sum_c e^(m_jc - m_j) l_jc,  o_j = sum_c e^(m_jc - m_j) o_jc,
+// in chunk order, and (m_j, l_j, o_j) is written to the workspace.  The output
+// is then formed from exactly the values written, so merge-and-combine gives
+// the same bytes as a merge followed by a combine of the workspace.
 //
-// The workload is small (NS KB per row) and latency-bound, so it is spread
-// wide: one workgroup per (row, quarter of the 256 dimensions), four waves per
-// workgroup.  Every wave reduces M over all splits itself (no barrier), then
-// wave v accumulates splits j = v, v+4, ... with each lane owning one dimension
-// and all of its loads issued before use; the four partial sums are added in
-// wave order through LDS.  Every sum has a fixed order, so results are
-// byte-deterministic.
+// The work is small (NS * C KB per row) and latency-bound, so it is spread
+// wide: one workgroup per (row, quarter of the 256 dimensions), eight waves.
+// Every wave reduces M over all states itself (no barrier), then wave v takes
+// splits j = v, v+8, ... with each lane owning one dimension and all loads of a
+// batch issued before use; the eight partial sums are added in wave order
+// through LDS.  Every sum has a fixed order, so results are byte-deterministic.
 #include "dfv_common.h"
 
 namespace dfv {
 namespace {
 
 constexpr float kNegInf = -__builtin_inff();
-constexpr int kChunk = 8;   // loads in flight per lane and batch
+constexpr int kCombineWaves = 8;
 
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
@@ -30,50 +35,81 @@ __device__ __forceinline__ float wave_max(float x) {
   return x;
 }
 
-__global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
-  __shared__ float s_num[kWaves][64];
-  __shared__ float s_den[kWaves];
+// C = chunks per split in the source (1: the source is the workspace itself).
+// OUT = form the FP16 output (else only merge chunk states into the workspace).
+template <int C, bool OUT>
+__global__ __launch_bounds__(kCombineWaves * 64) void combine_kernel(CombineArgs a) {
+  constexpr int kBatch = C == 1 ? 16 : (C == 2 ? 12 : 10);   // splits per wave per load batch
+  __shared__ float s_num[kCombineWaves][64];
+  __shared__ float s_den[kCombineWaves];
   const int row = blockIdx.x >> 2;
   const int quarter = blockIdx.x & 3;
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int NS = a.num_splits;
-  const float* mrow = a.ws_max + (size_t)row * NS;
-  const float* lrow = a.ws_sum + (size_t)row * NS;
-  const float* orow = a.ws_num + (size_t)row * NS * kHeadDim + 64 * quarter + lane;
+  const float* mrow = a.src_max + (size_t)row * NS * C;
+  const float* lrow = a.src_sum + (size_t)row * NS * C;
+  const float* orow = a.src_num + (size_t)row * NS * C * kHeadDim + 64 * quarter + lane;
 
   float M = kNegInf;
-  for (int j = lane; j < NS; j += 64) M = fmaxf(M, mrow[j]);
-  M = wave_max(M);
-
   float num = 0.f, den = 0.f;
-  if (M != kNegInf) {
-    for (int j0 = wave; j0 < NS; j0 += kWaves * kChunk) {
-      float ov[kChunk];
+  for (int j0 = wave; j0 < NS; j0 += kCombineWaves * kBatch) {
+    float mv[kBatch][C], lv[kBatch][C], ov[kBatch][C];
 #pragma unroll
-      for (int k = 0; k < kChunk; ++k) {
-        const int j = j0 + kWaves * k;
-        ov[k] = j < NS ? orow[(size_t)j * kHeadDim] : 0.f;
+    for (int k = 0; k < kBatch; ++k) {
+      const int j = j0 + kCombineWaves * k;
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        const bool in = j < NS;
+        const size_t s = (size_t)(in ? j : 0) * C + c;
+        ov[k][c] = orow[s * kHeadDim];
+        mv[k][c] = in ? mrow[s] : kNegInf;
+        lv[k][c] = lrow[s];
       }
+    }
+    if (OUT && j0 == wave) {   // row max over every state, while the batch is in flight
+      for (int j = lane; j < NS * C; j += 64) M = fmaxf(M, mrow[j]);
+      M = wave_max(M);
+    }
 #pragma unroll
-      for (int k = 0; k < kChunk; ++k) {
-        const int j = j0 + kWaves * k;
-        if (j < NS) {
-          const float mj = mrow[j];
-          const float e = (mj == kNegInf) ? 0.f : __expf(mj - M);
-          num += ov[k] * e;
-          den += lrow[j] * e;
+    for (int k = 0; k < kBatch; ++k) {
+      const int j = j0 + kCombineWaves * k;
+      float mj = mv[k][0], lj = lv[k][0], oj = ov[k][0];
+      if (C > 1) {
+#pragma unroll
+        for (int c = 1; c < C; ++c) mj = fmaxf(mj, mv[k][c]);
+        lj = 0.f;
+        oj = 0.f;
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+          const float e = (mv[k][c] == kNegInf) ? 0.f : __expf(mv[k][c] - mj);
+          lj = __builtin_fmaf(lv[k][c], e, lj);
+          oj = __builtin_fmaf(ov[k][c], e, oj);
         }
+        if (j < NS) {
+          const size_t w = (size_t)row * NS + j;
+          a.ws_num[w * kHeadDim + 64 * quarter + lane] = oj;
+          if (quarter == 0 && lane == 0) {
+            a.ws_max[w] = mj;
+            a.ws_sum[w] = lj;
+          }
+        }
+      }
+      if (OUT) {
+        const float e = (mj == kNegInf) ? 0.f : __expf(mj - M);
+        num = __builtin_fmaf(oj, e, num);
+        den = __builtin_fmaf(lj, e, den);
       }
     }
   }
+  if (!OUT) return;
   s_num[wave][lane] = num;
   if (lane == 0) s_den[wave] = den;
   __syncthreads();
   if (wave == 0) {
     float n = 0.f, d = 0.f;
 #pragma unroll
-    for (int v = 0; v < kWaves; ++v) {
+    for (int v = 0; v < kCombineWaves; ++v) {
       n += s_num[v][lane];
       d += s_den[v];
     }
@@ -81,10 +117,25 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
   }
 }
 
+template <int C>
+void launch_c(const CombineArgs& a, hipStream_t stream) {
+  const dim3 grid(4 * a.rows), block(kCombineWaves * 64);
+  if (a.out)
+    hipLaunchKernelGGL((combine_kernel<C, true>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((combine_kernel<C, false>), grid, block, 0, stream, a);
+}
+
 }  // namespace
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(combine_kernel, dim3(4 * a.rows), dim3(kThreads), 0, stream, a);
+  switch (a.chunks) {
+    case 1: launch_c<1>(a, stream); break;
+    case 2: launch_c<2>(a, stream); break;
+    case 3: launch_c<3>(a, stream); break;
+    case 4: launch_c<4>(a, stream); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

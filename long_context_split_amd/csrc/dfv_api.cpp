@@ -35,8 +35,11 @@ dfv_status check_desc(const dfv_attn_desc* d) {
   return DFV_OK;
 }
 
-// Scratch the kernels need: none (each split state is built inside one workgroup).
-size_t scratch_need(const dfv_attn_desc*) { return 0; }
+// Scratch the split kernel needs: the key-chunk states when a split is cut into
+// several chunks (zero otherwise).
+size_t scratch_need(const dfv_attn_desc* d) {
+  return dfv::scratch_bytes(d->batch, d->num_q, d->num_splits);
+}
 
 dfv_status check_split_ptrs(const void* q, const uint8_t* kc, const uint8_t* vc, const int32_t* bt,
                             const int32_t* cl, const float* ks, const float* vs, const float* wm,
@@ -55,12 +58,28 @@ dfv_status check_combine_ptrs(const float* wm, const float* wl, const float* wn,
   return DFV_OK;
 }
 
+// Where the chunk states of the split kernel live inside the scratch buffer.
+struct ChunkStates {
+  int chunks;
+  float* num;
+  float* max;
+  float* sum;
+};
+
+ChunkStates chunk_states(const dfv_attn_desc* d, void* scratch) {
+  ChunkStates c;
+  c.chunks = dfv::split_chunks(d->batch, d->num_splits);
+  const size_t n = dfv::scratch_floats(d->batch * d->num_q * dfv::kQHeads, d->num_splits, c.chunks);
+  c.num = (float*)scratch;
+  c.max = c.num ? c.num + n * kHeadDim : nullptr;
+  c.sum = c.max ? c.max + n : nullptr;
+  return c;
+}
+
 dfv_status launch_split_checked(const dfv_attn_desc* d, const void* q, const uint8_t* kc,
                                 const uint8_t* vc, const int32_t* bt, const int32_t* cl,
                                 const float* ks, const float* vs, float* wm, float* wl, float* wn,
-                                void* scratch, size_t scratch_bytes, hipStream_t stream) {
-  (void)scratch;
-  if (scratch_bytes < scratch_need(d)) return DFV_ERR_SCRATCH;
+                                const ChunkStates& cs, hipStream_t stream) {
   dfv::SplitArgs a;
   a.q = (const _Float16*)q;
   a.k_cache = kc;
@@ -69,9 +88,10 @@ dfv_status launch_split_checked(const dfv_attn_desc* d, const void* q, const uin
   a.context_lens = cl;
   a.k_scale = ks;
   a.v_scale = vs;
-  a.ws_max = wm;
-  a.ws_sum = wl;
-  a.ws_num = wn;
+  a.chunks = cs.chunks;
+  a.st_max = cs.chunks > 1 ? cs.max : wm;
+  a.st_sum = cs.chunks > 1 ? cs.sum : wl;
+  a.st_num = cs.chunks > 1 ? cs.num : wn;   // with one chunk the states are the workspace
   a.batch = d->batch;
   a.num_q = d->num_q;
   a.max_blocks = d->max_blocks_per_seq;
@@ -82,9 +102,17 @@ dfv_status launch_split_checked(const dfv_attn_desc* d, const void* q, const uin
   return dfv::launch_split(a, stream) == hipSuccess ? DFV_OK : DFV_ERR_LAUNCH;
 }
 
-dfv_status launch_combine_checked(const dfv_attn_desc* d, const float* wm, const float* wl,
-                                  const float* wn, void* out, hipStream_t stream) {
+// Merge of chunk states into the workspace (chunks > 1), and/or the combine
+// into `out` (out != NULL).  With chunks = 1 and out = NULL there is nothing
+// to do.
+dfv_status launch_combine_checked(const dfv_attn_desc* d, const ChunkStates& cs, float* wm, float* wl,
+                                  float* wn, void* out, hipStream_t stream) {
+  if (cs.chunks == 1 && !out) return DFV_OK;
   dfv::CombineArgs a;
+  a.chunks = cs.chunks;
+  a.src_max = cs.chunks > 1 ? cs.max : wm;
+  a.src_sum = cs.chunks > 1 ? cs.sum : wl;
+  a.src_num = cs.chunks > 1 ? cs.num : wn;
   a.ws_max = wm;
   a.ws_sum = wl;
   a.ws_num = wn;
@@ -131,8 +159,35 @@ dfv_status dfv_attn_split(const dfv_attn_desc* desc, const void* q, const uint8_
   s = check_split_ptrs(q, k_cache, v_cache, block_table, context_lens, k_scale, v_scale, ws_max,
                        ws_sum, ws_num, scratch);
   if (s != DFV_OK) return s;
+  if (scratch_bytes < scratch_need(desc) || (scratch_need(desc) && !scratch)) return DFV_ERR_SCRATCH;
+  const ChunkStates cs = chunk_states(desc, scratch);
+  s = launch_split_checked(desc, q, k_cache, v_cache, block_table, context_lens, k_scale, v_scale,
+                           ws_max, ws_sum, ws_num, cs, (hipStream_t)stream);
+  if (s != DFV_OK) return s;
+  return launch_combine_checked(desc, cs, ws_max, ws_sum, ws_num, nullptr, (hipStream_t)stream);
+}
+
+dfv_status dfv_attn_chunks(const dfv_attn_desc* desc, int32_t* chunks) {
+  if (!chunks) return DFV_ERR_NULL;
+  *chunks = 0;
+  const dfv_status s = check_desc(desc);
+  if (s == DFV_OK) *chunks = dfv::split_chunks(desc->batch, desc->num_splits);
+  return s;
+}
+
+dfv_status dfv_attn_split_chunks(const dfv_attn_desc* desc, const void* q, const uint8_t* k_cache,
+                                 const uint8_t* v_cache, const int32_t* block_table,
+                                 const int32_t* context_lens, const float* k_scale,
+                                 const float* v_scale, float* chunk_max, float* chunk_sum,
+                                 float* chunk_num, void* stream) {
+  dfv_status s = check_desc(desc);
+  if (s != DFV_OK) return s;
+  s = check_split_ptrs(q, k_cache, v_cache, block_table, context_lens, k_scale, v_scale, chunk_max,
+                       chunk_sum, chunk_num, nullptr);
+  if (s != DFV_OK) return s;
+  ChunkStates cs{dfv::split_chunks(desc->batch, desc->num_splits), chunk_num, chunk_max, chunk_sum};
   return launch_split_checked(desc, q, k_cache, v_cache, block_table, context_lens, k_scale, v_scale,
-                              ws_max, ws_sum, ws_num, scratch, scratch_bytes, (hipStream_t)stream);
+                              chunk_max, chunk_sum, chunk_num, cs, (hipStream_t)stream);
 }
 
 dfv_status dfv_attn_combine(const dfv_attn_desc* desc, const float* ws_max, const float* ws_sum,
@@ -141,7 +196,10 @@ dfv_status dfv_attn_combine(const dfv_attn_desc* desc, const float* ws_max, cons
   if (s != DFV_OK) return s;
   s = check_combine_ptrs(ws_max, ws_sum, ws_num, out);
   if (s != DFV_OK) return s;
-  return launch_combine_checked(desc, ws_max, ws_sum, ws_num, out, (hipStream_t)stream);
+  ChunkStates cs{1, nullptr, nullptr, nullptr};
+  // With one chunk the workspace is only read.
+  return launch_combine_checked(desc, cs, (float*)ws_max, (float*)ws_sum, (float*)ws_num, out,
+                                (hipStream_t)stream);
 }
 
 dfv_status dfv_attn(const dfv_attn_desc* desc, const void* q, const uint8_t* k_cache,
@@ -155,11 +213,12 @@ dfv_status dfv_attn(const dfv_attn_desc* desc, const void* q, const uint8_t* k_c
   if (s != DFV_OK) return s;
   s = check_combine_ptrs(ws_max, ws_sum, ws_num, out);
   if (s != DFV_OK) return s;
-  if (scratch_bytes < scratch_need(desc)) return DFV_ERR_SCRATCH;
+  if (scratch_bytes < scratch_need(desc) || (scratch_need(desc) && !scratch)) return DFV_ERR_SCRATCH;
+  const ChunkStates cs = chunk_states(desc, scratch);
   s = launch_split_checked(desc, q, k_cache, v_cache, block_table, context_lens, k_scale, v_scale,
-                           ws_max, ws_sum, ws_num, scratch, scratch_bytes, (hipStream_t)stream);
+                           ws_max, ws_sum, ws_num, cs, (hipStream_t)stream);
   if (s != DFV_OK) return s;
-  return launch_combine_checked(desc, ws_max, ws_sum, ws_num, out, (hipStream_t)stream);
+  return launch_combine_checked(desc, cs, ws_max, ws_sum, ws_num, out, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -16,7 +16,10 @@ constexpr int kQHeads = 6;
 constexpr int kPage = 16;                       // tokens per KV page
 constexpr int kTile = 32;                       // keys per online-softmax update ([#587] Implementation: N32)
 constexpr int kMaxQ = 8;
+constexpr int kMaxRows = kMaxQ * kQHeads;       // 48 query rows = three 16-row MFMA blocks
 constexpr int kMaxSplits = 256;
+constexpr int kTargetCUs = 256;                 // MI355X compute units (sizes the key chunking)
+constexpr int kMaxChunks = 4;                   // key chunks per logical split, at most
 constexpr int kWaves = 4;                       // one wave per SIMD
 constexpr int kThreads = kWaves * 64;
 constexpr int kPageBytes = kPage * kHeadDim;    // 4096 B of E4M3 per page per cache
@@ -32,9 +35,12 @@ struct SplitArgs {
   const int32_t* context_lens;
   const float* k_scale;
   const float* v_scale;
-  float* ws_max;
-  float* ws_sum;
-  float* ws_num;
+  // Where the states go: the workspace itself (chunks = 1) or scratch laid out
+  // as the workspace with the chunk index innermost (chunks > 1).
+  float* st_max;      // [rows][NS][chunks]
+  float* st_sum;      // [rows][NS][chunks]
+  float* st_num;      // [rows][NS][chunks][256]
+  int chunks;         // key chunks per logical split
   int batch;
   int num_q;
   int max_blocks;
@@ -45,14 +51,33 @@ struct SplitArgs {
 };
 
 struct CombineArgs {
-  const float* ws_max;
-  const float* ws_sum;
-  const float* ws_num;
-  _Float16* out;
+  // Source states: the workspace (chunks = 1) or the split kernel's chunk
+  // states in scratch (chunks > 1).
+  const float* src_max;
+  const float* src_sum;
+  const float* src_num;
+  int chunks;
+  // Merged workspace, written only when chunks > 1.
+  float* ws_max;
+  float* ws_sum;
+  float* ws_num;
+  _Float16* out;      // NULL: merge only (no output)
   int rows;           // batch * num_q * 6
   int num_splits;
 };
 
+int split_chunks(int batch, int num_splits);
+
+// Scratch (chunks > 1): chunk numerators, then maxima, then sums.
+inline size_t scratch_floats(int rows, int num_splits, int chunks) {
+  return (size_t)rows * num_splits * chunks;
+}
+inline size_t scratch_bytes(int batch, int num_q, int num_splits) {
+  const int chunks = split_chunks(batch, num_splits);
+  if (chunks == 1) return 0;
+  const size_t n = scratch_floats(batch * num_q * kQHeads, num_splits, chunks);
+  return (n * (kHeadDim + 2) * sizeof(float) + 255) & ~(size_t)255;
+}
 int split_grid(int batch, int num_q, int num_splits);
 hipError_t launch_split(const SplitArgs& a, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);

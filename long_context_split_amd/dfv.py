@@ -17,8 +17,8 @@ LIB_PATH = os.path.join(PKG, "libdfv.so")
 DFV_OK = 0
 STATUS = {0: "DFV_OK", -1: "DFV_ERR_NULL", -2: "DFV_ERR_UNSUPPORTED", -3: "DFV_ERR_ALIGN",
           -4: "DFV_ERR_ARG", -5: "DFV_ERR_LAUNCH", -7: "DFV_ERR_SCRATCH"}
-ENTRY_POINTS = ("dfv_status_string", "dfv_attn_check", "dfv_attn_scratch_bytes", "dfv_attn_split",
-                "dfv_attn_combine", "dfv_attn")
+ENTRY_POINTS = ("dfv_status_string", "dfv_attn_check", "dfv_attn_scratch_bytes", "dfv_attn_chunks",
+                "dfv_attn_split_chunks", "dfv_attn_split", "dfv_attn_combine", "dfv_attn")
 
 
 class DfvError(RuntimeError):
@@ -53,6 +53,10 @@ def lib():
         L.dfv_attn_check.restype = ctypes.c_int
         L.dfv_attn_scratch_bytes.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(ctypes.c_size_t)]
         L.dfv_attn_scratch_bytes.restype = ctypes.c_int
+        L.dfv_attn_chunks.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(ctypes.c_int32)]
+        L.dfv_attn_chunks.restype = ctypes.c_int
+        L.dfv_attn_split_chunks.argtypes = [ctypes.POINTER(Desc)] + [_P] * 10 + [_P]
+        L.dfv_attn_split_chunks.restype = ctypes.c_int
         L.dfv_attn_split.argtypes = [ctypes.POINTER(Desc)] + [_P] * 10 + [_P, ctypes.c_size_t, _P]
         L.dfv_attn_split.restype = ctypes.c_int
         L.dfv_attn_combine.argtypes = [ctypes.POINTER(Desc), _P, _P, _P, _P, _P]
@@ -77,6 +81,12 @@ def check(desc: Desc) -> int:
 def scratch_bytes(desc: Desc) -> int:
     n = ctypes.c_size_t(0)
     _raise(lib().dfv_attn_scratch_bytes(ctypes.byref(desc), ctypes.byref(n)), "dfv_attn_scratch_bytes")
+    return int(n.value)
+
+
+def chunks(desc: Desc) -> int:
+    n = ctypes.c_int32(0)
+    _raise(lib().dfv_attn_chunks(ctypes.byref(desc), ctypes.byref(n)), "dfv_attn_chunks")
     return int(n.value)
 
 
@@ -114,7 +124,7 @@ class Workspace:
             ws_max=torch.empty(*rows, desc.num_splits, dtype=torch.float32, device=device),
             ws_sum=torch.empty(*rows, desc.num_splits, dtype=torch.float32, device=device),
             ws_num=torch.empty(*rows, desc.num_splits, desc.head_dim, dtype=torch.float32, device=device),
-            scratch=torch.zeros(nbytes, dtype=torch.uint8, device=device) if nbytes else None,
+            scratch=torch.empty(nbytes, dtype=torch.uint8, device=device) if nbytes else None,
             out=torch.empty(*rows, desc.head_dim, dtype=torch.float16, device=device))
 
 
@@ -126,6 +136,24 @@ def attn_split(desc: Desc, q, k_cache, v_cache, block_table, context_lens, k_sca
                               0 if scratch is None else scratch.numel() * scratch.element_size(),
                               _stream(stream))
     _raise(st, "dfv_attn_split")
+
+
+def attn_split_chunks(desc: Desc, q, k_cache, v_cache, block_table, context_lens, k_scale, v_scale,
+                      chunk_max, chunk_sum, chunk_num, stream=None):
+    st = lib().dfv_attn_split_chunks(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                     _ptr(block_table), _ptr(context_lens), _ptr(k_scale), _ptr(v_scale),
+                                     _ptr(chunk_max), _ptr(chunk_sum), _ptr(chunk_num), _stream(stream))
+    _raise(st, "dfv_attn_split_chunks")
+
+
+def chunk_buffers(desc: Desc, device="cuda"):
+    """(chunk_max, chunk_sum, chunk_num) torch tensors for dfv_attn_split_chunks."""
+    import torch
+    c = chunks(desc)
+    rows = (desc.batch, desc.num_q, desc.num_q_heads, desc.num_splits, c)
+    return (torch.empty(*rows, dtype=torch.float32, device=device),
+            torch.empty(*rows, dtype=torch.float32, device=device),
+            torch.empty(*rows, desc.head_dim, dtype=torch.float32, device=device))
 
 
 def attn_combine(desc: Desc, ws_max, ws_sum, ws_num, out, stream=None):

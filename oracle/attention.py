@@ -225,14 +225,14 @@ def reference_rows_at(q, k_cache, v_cache, block_table, context_lens, k_scale, v
     return np.stack(res)
 
 
-def split_state_at(q, k_cache, v_cache, block_table, context_lens, k_scale, v_scale,
-                   softmax_scale, b: int, i: int, h: int, j: int, num_splits: int = NUM_SPLITS,
-                   split_size: int = 0):
-    """State (m, l, o[D]) of one (b, i, h, split j), computed on its own (sampled checks)."""
+def range_state_at(q, k_cache, v_cache, block_table, context_lens, k_scale, v_scale,
+                   softmax_scale, b: int, i: int, h: int, lo: int, hi: int):
+    """State (m, l, o[D]) of row (b, i, h) over the keys [lo, hi) it may see, i.e.
+    [lo, min(hi, p_i + 1)): the same per-split state definition ([#587]
+    Implementation; [#589] Test Plan) applied to an arbitrary key range."""
     L = int(context_lens[b])
-    S = split_size if split_size else split_tokens(L, num_splits)
     pos = query_positions(L, q.shape[1])
-    lo, hi = j * S, min((j + 1) * S, int(pos[i]) + 1)
+    hi = min(hi, int(pos[i]) + 1)
     d = q.shape[3]
     if lo >= hi:
         return -math.inf, 0.0, np.zeros(d)
@@ -247,3 +247,13 @@ def split_state_at(q, k_cache, v_cache, block_table, context_lens, k_scale, v_sc
     mj = s.max()
     w = np.exp(s - mj)
     return mj, w.sum(), float(np.float64(v_scale)) * (w @ v_hat)
+
+
+def split_state_at(q, k_cache, v_cache, block_table, context_lens, k_scale, v_scale,
+                   softmax_scale, b: int, i: int, h: int, j: int, num_splits: int = NUM_SPLITS,
+                   split_size: int = 0):
+    """State (m, l, o[D]) of one (b, i, h, split j), computed on its own (sampled checks)."""
+    L = int(context_lens[b])
+    S = split_size if split_size else split_tokens(L, num_splits)
+    return range_state_at(q, k_cache, v_cache, block_table, context_lens, k_scale, v_scale,
+                          softmax_scale, b, i, h, j * S, (j + 1) * S)

@@ -69,9 +69,19 @@ def test_fixed_split_must_cover_context(L):
     assert dfv.check(_good(split_tokens=3264)) == -4         # 80 * 3264 <  261888
 
 
-def test_scratch_size_is_zero_and_reported_through_out_parameter(L):
+def test_scratch_size_reported_through_out_parameter(L):
+    # one sequence, q8 (48 rows), 80 splits -> 3 key chunks per split: 48*80*3
+    # chunk states of 256 + 2 floats, rounded up to a multiple of 256 bytes
     d = _good()
-    assert dfv.scratch_bytes(d) == 0
+    assert dfv.scratch_bytes(d) == 48 * 80 * 3 * 258 * 4
+    # q1: 6 rows
+    assert dfv.scratch_bytes(_good(num_q=1)) == 6 * 80 * 3 * 258 * 4
+    # 4 sequences x 80 splits fill the machine with one chunk each: no scratch
+    assert dfv.scratch_bytes(_good(batch=4)) == 0
+    # few splits: at most 4 chunks; q3 x 2 splits x 4 chunks = 144 states, rounded
+    n3 = 18 * 2 * 4 * 258 * 4
+    assert dfv.scratch_bytes(_good(num_q=3, num_splits=2, max_context_len=4096, max_blocks=256)) == \
+        (n3 + 255) // 256 * 256
     n = ctypes.c_size_t(123)
     d.num_q_heads = 4
     assert L.dfv_attn_scratch_bytes(ctypes.byref(d), ctypes.byref(n)) == -2 and n.value == 0
@@ -93,7 +103,10 @@ def test_null_and_misaligned_pointers_are_refused_before_launch(L):
     st = L.dfv_attn_split(ctypes.byref(d), *args, None, 0, None)
     assert st == -1
     # misaligned scratch
-    assert L.dfv_attn_split(ctypes.byref(d), *ok, P(4096 + 8), 0, None) == -3
+    assert L.dfv_attn_split(ctypes.byref(d), *ok, P(4096 + 8), 1 << 30, None) == -3
+    # scratch too small, or missing, when the descriptor needs some
+    assert L.dfv_attn_split(ctypes.byref(d), *ok, P(1 << 20), 100, None) == -7
+    assert L.dfv_attn_split(ctypes.byref(d), *ok, None, 1 << 30, None) == -7
     # misaligned q
     args = list(ok)
     args[0] = P(4096 + 2)
@@ -112,3 +125,26 @@ def test_binding_raises_when_library_missing(monkeypatch, tmp_path):
     monkeypatch.setattr(dfv, "LIB_PATH", str(tmp_path / "libdfv.so"))
     with pytest.raises(FileNotFoundError):
         dfv.lib()
+
+
+def test_chunk_count(L):
+    assert dfv.chunks(_good()) == 3                       # 256 // 80
+    assert dfv.chunks(_good(batch=4)) == 1
+    assert dfv.chunks(_good(num_splits=2, max_context_len=4096, max_blocks=256)) == 4
+    assert dfv.chunks(_good(batch=2, num_splits=64)) == 2
+    n = ctypes.c_int32(7)
+    assert L.dfv_attn_chunks(ctypes.byref(_good(num_q=0)), ctypes.byref(n)) == -2 and n.value == 0
+    assert L.dfv_attn_chunks(ctypes.byref(_good()), None) == -1
+
+
+def test_split_chunks_refuses_bad_arguments_before_launch(L):
+    d = _good()
+    P = ctypes.c_void_p
+    ok = [P(4096 * (i + 1)) for i in range(10)]
+    args = list(ok)
+    args[8] = None                                        # chunk_sum
+    assert L.dfv_attn_split_chunks(ctypes.byref(d), *args, None) == -1
+    args = list(ok)
+    args[9] = P(4096 * 10 + 4)                            # chunk_num misaligned
+    assert L.dfv_attn_split_chunks(ctypes.byref(d), *args, None) == -3
+    assert L.dfv_attn_split_chunks(ctypes.byref(_good(head_dim=128)), *ok, None) == -2

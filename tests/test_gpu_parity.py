@@ -228,3 +228,45 @@ def test_full_size_sampled(name, layer):
         check_ws(res["ws_max"][0, i, h, j][None], res["ws_sum"][0, i, h, j][None],
                  res["ws_num"][0, i, h, j][None], np.array([mj]), np.array([lj]), oj[None])
     assert np.all(np.isfinite(res["out"]))
+
+
+def _chunk_ranges(L, ns, C, split_tokens=0):
+    """Key range [lo, hi) of every (split j, chunk c), restating the layout that
+    dfv_attn_split_chunks documents: tiles of 32 keys cut per split, then into
+    C near-equal runs of whole tiles."""
+    S = split_tokens if split_tokens else A.split_tokens(L, ns)
+    T = -(-L // 32)
+    out = {}
+    for j in range(ns):
+        a, b = min(j * S // 32, T), min((j + 1) * S // 32, T)
+        n = b - a
+        for c in range(C):
+            out[j, c] = (32 * (a + (c * n) // C), 32 * (a + ((c + 1) * n) // C))
+    return out
+
+
+@pytest.mark.parametrize("lens,nq,ns", [([4096], 8, 80), ([20000], 5, 80), ([1500], 1, 40)])
+def test_chunk_states_match_oracle_key_ranges(lens, nq, ns):
+    inp = _layer(lens, nq, seed=1200 + nq)
+    _note(f"split_chunks L={lens} q{nq} ns={ns}")
+    desc = dfv.desc_for(inp, num_splits=ns)
+    C = dfv.chunks(desc)
+    assert C > 1
+    cm, cl, cn = dfv.chunk_buffers(desc)
+    dfv.attn_split_chunks(desc, inp.q, inp.k_cache, inp.v_cache, inp.block_table, inp.context_lens,
+                          inp.k_scale, inp.v_scale, cm, cl, cn)
+    torch.cuda.synchronize()
+    gm, gl, gn = cm.cpu().numpy(), cl.cpu().numpy(), cn.cpu().numpy()
+    d = inp.numpy()
+    a = (d["q"], d["k_cache"], d["v_cache"], d["block_table"], d["context_lens"], d["k_scale"],
+         d["v_scale"], d["softmax_scale"])
+    ranges = _chunk_ranges(lens[0], ns, C)
+    m = np.empty((1, nq, 6, ns, C))
+    l = np.empty_like(m)
+    o = np.empty((1, nq, 6, ns, C, 256))
+    for i in range(nq):
+        for h in range(6):
+            for (j, c), (lo, hi) in ranges.items():
+                m[0, i, h, j, c], l[0, i, h, j, c], o[0, i, h, j, c] = A.range_state_at(
+                    *a, b=0, i=i, h=h, lo=lo, hi=hi)
+    check_ws(gm, gl, gn, m, l, o)

@@ -272,3 +272,29 @@ def test_sampled_helpers_match_full_oracle():
         assert (mj == m[0, i, h, j]) or abs(mj - m[0, i, h, j]) <= 1e-13 * max(1, abs(mj))
         assert lj == pytest.approx(l[0, i, h, j], rel=1e-13, abs=0)
         assert rel_err(oj, o[0, i, h, j]) <= 1e-13 if np.any(oj) else np.all(o[0, i, h, j] == 0)
+
+
+def test_range_state_matches_brute_force_per_key_states():
+    # Per-key states from the pure-Python brute force (split size 1: m = s_t,
+    # l = 1, o = v_scale * V_t) merged by hand over arbitrary key ranges must
+    # equal the oracle's state of that range (cut at each row's causal bound).
+    dat = layer_np([45], 3, seed=41, head_dim=16)
+    a = args(dat)
+    _, bm, bl, bo = brute.brute_force(*a, num_splits=45, split_size=1)
+    bm = np.array(bm)
+    bo = np.array(bo)
+    pos = A.query_positions(45, 3)
+    for (lo, hi) in [(0, 45), (0, 1), (7, 19), (19, 43), (40, 45), (44, 60), (43, 43)]:
+        for i in range(3):
+            for h in (0, 5):
+                m, l, o = A.range_state_at(*a, b=0, i=i, h=h, lo=lo, hi=hi)
+                top = min(hi, int(pos[i]) + 1)
+                if lo >= top:
+                    assert m == -math.inf and l == 0.0 and not np.any(o)
+                    continue
+                ms = bm[0, i, h, lo:top]
+                mref = ms.max()
+                w = np.exp(ms - mref)
+                assert m == pytest.approx(mref, rel=1e-13, abs=1e-13)
+                assert l == pytest.approx(math.fsum(w), rel=1e-12)
+                assert rel_err(o, (w[:, None] * bo[0, i, h, lo:top]).sum(0)) <= 1e-12
