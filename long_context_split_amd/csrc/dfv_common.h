@@ -14,7 +14,7 @@ namespace dfv {
 constexpr int kHeadDim = 256;
 constexpr int kQHeads = 6;
 constexpr int kPage = 16;                       // tokens per KV page
-constexpr int kTile = 32;                       // keys per online-softmax update ([#587] Implementation: N32)
+constexpr int kTile = 32;                       // split boundaries fall on 32-key tiles ([#587] Implementation: N32)
 constexpr int kMaxQ = 8;
 constexpr int kMaxRows = kMaxQ * kQHeads;       // 48 query rows = three 16-row MFMA blocks
 constexpr int kMaxSplits = 256;
@@ -23,8 +23,6 @@ constexpr int kMaxChunks = 4;                   // key chunks per logical split,
 constexpr int kWaves = 4;                       // one wave per SIMD
 constexpr int kThreads = kWaves * 64;
 constexpr int kPageBytes = kPage * kHeadDim;    // 4096 B of E4M3 per page per cache
-constexpr int kStageBytes = 4 * kPageBytes;     // K pages 0,1 then V pages 0,1 of one tile
-constexpr int kStageArray = kWaves * kStageBytes;   // one LDS array per pipeline stage
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct SplitArgs {

@@ -5,47 +5,45 @@
 //   [#589] "[Perf] Reduce DFlash2 attention cost and screen exact QK reuse"
 //
 // What one launch computes: for every sequence b, query row r = 6*i + h and
-// logical split j, the FP32 state (max, sum, numerator) of causal softmax
-// attention restricted to the split's keys ([#587] Implementation: 80 logical
-// splits, N32 online updates, compensated FP32 sums, probability residual
-// products, FP32 state; [#589] Test Plan: the full FP32 workspace is output).
+// logical split j (or key chunk of a split), the FP32 state (max, sum,
+// numerator) of causal softmax attention restricted to those keys ([#587]
+// Implementation: 80 logical splits, compensated FP32 sums, probability
+// residual products, FP32 state; [#589] Test Plan: the FP32 workspace is an
+// output).
 //
 // Work decomposition (MI355X: 256 CUs in 8 XCDs, 64-wide waves, 160 KB LDS/CU):
 //   * Each logical split is cut into C key chunks (C = 3 for one sequence and
 //     80 splits: 240 workgroups, about one per CU).  Workgroups never talk to
 //     each other: with C = 1 a workgroup writes its split's workspace entry,
-//     with C > 1 it writes its chunk state to scratch and a separate merge
-//     pass (fused into the combine kernel when the output is wanted) reduces
-//     the C states of a split in chunk order, so results are deterministic.
-//   * Four waves (one per SIMD) take the chunk's 32-key tiles in turn.  Each
-//     wave owns all 6q query rows (up to three 16-row blocks), so every K and V
-//     byte is decoded once and each decoded K fragment feeds every row block
-//     (the pages' reuse of one K fragment across three M16 products, [#589]
-//     Purpose).
-//   * Each wave streams its tiles through a private two-stage LDS ring with
-//     16-byte direct-to-LDS loads (global_load_lds_dwordx4); one 4 KB page is four
-//     fully coalesced wave instructions.  Inside a 256-byte token row the 16-byte
-//     chunks are XOR-swizzled by the row's page slot so operand reads from LDS
-//     are bank-conflict free.
-//   * QK^T runs as S^T = K * Q^T on v_mfma_f32_16x16x32_f16 (A = 16 keys x 32
-//     dims of K, B = 32 dims x 16 rows of Q, staged once in LDS in operand
-//     order).  The C layout leaves each lane 4 keys of one row, so a row max is
-//     an in-lane max plus two cross-lane steps (permlane16/32 swaps).
-//   * Each wave fixes a per-row reference max at the first tile where the row
-//     sees a key and never rescales its accumulators inside the tile loop.
-//     P = exp(s - m_ref) * 2^3 is carried as FP16 hi + FP16 lo (the pages'
-//     probability residual products, ~22 bits of P); should a row's running max
-//     outgrow its reference by more than 2^12 (beyond FP16 range for P), the
-//     wave raises the reference and redoes its tiles, which only strongly
-//     growing scores trigger.  The folds renormalise every state to its true
-//     max.  This is an exact re-association of the pages' 32-key online update;
-//     it is used because a data-dependent rescale of the AGPR accumulators makes
-//     the compiler shadow them in VGPRs.
-//   * PV runs as O^T += V^T * P^T on the same MFMA; the V operand (8 keys of one
-//     dimension per lane) comes straight out of LDS with the transposing read
-//     ds_read_b64_tr_b8.
-//   * The four wave states are folded in LDS as a reduce-scatter: afterwards
-//     wave v holds dimensions 64v..64v+63 of all rows, merged in wave order.
+//     with C > 1 it writes its chunk state and a separate merge pass (fused
+//     into the combine kernel when the output is wanted) reduces the C states
+//     of a split in chunk order, so results are deterministic.
+//   * A workgroup walks its chunk in 64-key tiles, four 16-token pages, through
+//     a four-stage LDS ring fed by 16-byte direct-to-LDS loads
+//     (global_load_lds_dwordx4); three tiles are in flight while one is
+//     computed.  Inside a 256-byte token row the 16-byte chunks are
+//     XOR-swizzled by the row's page slot so operand reads are conflict free.
+//   * The four waves (one per SIMD) split each tile by role.  For QK^T wave w
+//     takes page w: S^T = K_w * Q^T on v_mfma_f32_16x16x32_f16 for all 6q rows
+//     (up to three 16-row blocks, Q held in registers), so every K byte is
+//     decoded once and each decoded K fragment feeds every row block (the
+//     pages' reuse of one K fragment across three M16 products, [#589]
+//     Purpose).  Each wave turns its scores into P = exp(s - m_ref) * 2^3 as
+//     FP16 hi + FP16 lo (the pages' probability residual products, ~22 bits)
+//     and publishes them in LDS; after one barrier per tile, wave w forms
+//     O^T += V^T * P^T for its own 64 of the 256 dimensions over all 64 keys,
+//     with the V operand read straight out of LDS by the transposing
+//     ds_read_b64_tr_b8.  No wave ever holds another wave's dimensions, so
+//     there is nothing to fold at the end.
+//   * m_ref is a per-row reference max shared by the four waves: the max of
+//     the chunk's first tile (every row that sees any key of the chunk sees
+//     its first key).  Accumulators are never rescaled in the tile loop.
+//     Should a row's scores outgrow the reference by more than 2^12 (beyond
+//     FP16 range for P), the workgroup notices at the end of the chunk, takes
+//     the chunk's true row max as the reference and redoes the chunk once;
+//     only strongly growing scores trigger this.  The
+//     end of the chunk renormalises to the true max.  This is an exact
+//     re-association of the pages' 32-key online update.
 //   * E4M3 is decoded in registers with v_cvt_scalef32_pk_f16_fp8 (OCP on gfx950,
 //     two codes per instruction, exact in FP16).  The per-tensor scales are not
 //     applied during decode: k_scale is folded into the score scale and v_scale
@@ -56,6 +54,7 @@ namespace dfv {
 namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 typedef int int2v __attribute__((ext_vector_type(2)));
@@ -66,7 +65,14 @@ typedef unsigned uint2v __attribute__((ext_vector_type(2)));
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kPScale = 8.0f;              // 2^3: P * 2^3 <= 2^15 keeps FP16 hi finite
-constexpr float kRestartLog2 = 12.0f;        // P may reach 2^12 before a wave restarts
+constexpr float kPScaleLog2 = 3.0f;
+constexpr float kRestartLog2 = 12.0f;        // P may reach 2^12 before the workgroup restarts
+constexpr int kMaxRB = kMaxRows / 16;        // three 16-row blocks
+constexpr int kTileKeys = 64;                // one 16-token page per wave
+constexpr int kStages = 4;                   // LDS ring depth
+constexpr int kTileBytes = 8 * kPageBytes;   // K pages 0..3, then V pages 0..3 (32 KB)
+constexpr int kVOffset = 4 * kPageBytes;
+constexpr int kPSlot = 64 * 16;              // one (k-step, row block, hi|lo) P operand: 64 lanes x 16 B
 
 // Eight E4M3 codes (two dwords) to eight FP16 values, two codes per instruction.
 __device__ __forceinline__ half8 decode8(unsigned lo, unsigned hi) {
@@ -111,189 +117,41 @@ __device__ __forceinline__ void comp_add(float& sum, float& comp, float x) {
 // the tile loop waits on vmcnt itself (vector loads complete in order, so extra
 // outstanding loads only ever make the compiler's own waits stricter).  s_nop
 // covers the M0 write -> LDS-DMA wait state.
-__device__ __forceinline__ void lds_dma16(const uint8_t* base, unsigned off, LDS_AS uint8_t* dst) {
+__device__ __forceinline__ void lds_dma16(const void* base, unsigned off, LDS_AS uint8_t* dst) {
   const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)dst);
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :: "v"(off), "s"(base), "s"(m0) : "memory", "m0");
 }
 
+// 4-byte direct-to-LDS load: lane l's dword lands at dst + 4*l.
+__device__ __forceinline__ void lds_dma4(const void* base, unsigned off, LDS_AS void* dst) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)dst);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+               :: "v"(off), "s"(base), "s"(m0) : "memory", "m0");
+}
+
 // a ^ k computed in the loop body.  The swizzled LDS addresses of a tile are
 // loop-invariant; left to itself the compiler hoists all of them out of the
-// tile loop and spills them, and every spill reload waits for in-flight DMAs.
+// tile loop and keeps them in registers the loop needs for operands.
 __device__ __forceinline__ unsigned xor_in_loop(unsigned a, unsigned k) {
   unsigned r;
   asm volatile("v_xor_b32 %0, %1, %2" : "=v"(r) : "s"(k), "v"(a));
   return r;
 }
 
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+// Wait until at most `pending` (0, 8 or 16) of this wave's LDS loads are in flight.
+__device__ __forceinline__ void wait_dma(int pending) {
+  if (pending >= 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  else if (pending >= 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-// Issue the 16 direct-to-LDS loads of one 32-key tile (K pages 0,1 then V pages
-// 0,1).  Lane l of load qq fills LDS row r = 4*qq + l/16, chunk position l%16,
-// with global chunk (l%16) ^ r of that row.
-__device__ __forceinline__ void issue_tile(const uint8_t* kc, const uint8_t* vc, int page0, int page1,
-                                           LDS_AS uint8_t* dst, const unsigned (&lane_off)[4]) {
-  const uint8_t* k0 = kc + (size_t)page0 * kPageBytes;
-  const uint8_t* k1 = kc + (size_t)page1 * kPageBytes;
-  const uint8_t* v0 = vc + (size_t)page0 * kPageBytes;
-  const uint8_t* v1 = vc + (size_t)page1 * kPageBytes;
-#pragma unroll
-  for (int qq = 0; qq < 4; ++qq) {
-    lds_dma16(k0, lane_off[qq], dst + 0 * kPageBytes + qq * 1024);
-    lds_dma16(k1, lane_off[qq], dst + 1 * kPageBytes + qq * 1024);
-    lds_dma16(v0, lane_off[qq], dst + 2 * kPageBytes + qq * 1024);
-    lds_dma16(v1, lane_off[qq], dst + 3 * kPageBytes + qq * 1024);
-  }
-}
-
-// Per-wave softmax state for RB 16-row blocks; lane (n, g) owns row 16rb + n.
-template <int RB>
-struct WaveState {
-  float4v o[16][RB];   // O^T accumulators (x 2^3, relative to m_ref): dims 16mb + 4g + 0..3
-  float m_ref[RB];     // reference max (raw dot-product units); -inf until the row sees a key
-  float m_max[RB];     // true running max (raw units)
-  float l_sum[RB];     // this lane's compensated partial sum of P (relative to m_ref)
-  float l_cmp[RB];
-};
-
-template <int RB>
-__device__ __forceinline__ void state_reset(WaveState<RB>& st) {
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    st.m_ref[rb] = kNegInf;
-    st.m_max[rb] = kNegInf;
-    st.l_sum[rb] = 0.f;
-    st.l_cmp[rb] = 0.f;
-#pragma unroll
-    for (int mb = 0; mb < 16; ++mb) st.o[mb][rb] = float4v{0.f, 0.f, 0.f, 0.f};
-  }
-}
-
-// One 32-key tile: QK^T, softmax against the fixed reference max, PV with
-// P = hi + lo.  Returns true (before touching O) when some row max has outgrown
-// its reference by more than 2^kRestartLog2; the caller then restarts.
-// `masked` tiles hold keys past some row's causal bound or past L.
-// qlane points at this lane's Q fragments in LDS: fragment (rb, m) holds
-// Q[row 16rb+n][64g + 8m + 0..7] at qlane + (rb*8 + m)*1024.
-template <int RB>
-__device__ __forceinline__ bool compute_tile(WaveState<RB>& st, const LDS_AS uint8_t* qlane,
-                                             const LDS_AS uint8_t* kl, int t0, int L,
-                                             const int (&limit)[RB], bool masked, float c2, int n, int g) {
-  const LDS_AS uint8_t* vl = kl + 2 * kPageBytes;
-  // ---- S^T = K * Q^T for the tile's two 16-key blocks and every row block
-  float4v sacc[2][RB];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) sacc[kb][rb] = float4v{0.f, 0.f, 0.f, 0.f};
-  const LDS_AS uint8_t* krow0 = kl + n * 256;
-  const LDS_AS uint8_t* krow1 = kl + kPageBytes + n * 256;
-  uint4v kr0 = *(const LDS_AS uint4v*)(krow0 + 16 * ((4 * g) ^ n));
-  uint4v kr1 = *(const LDS_AS uint4v*)(krow1 + 16 * ((4 * g) ^ n));
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint4v c0 = kr0, c1 = kr1;
-    if (i < 3) {   // prefetch the next 16-byte chunk of both key rows
-      const int chunk = 16 * ((4 * g + i + 1) ^ n);
-      kr0 = *(const LDS_AS uint4v*)(krow0 + chunk);
-      kr1 = *(const LDS_AS uint4v*)(krow1 + chunk);
-    }
-    const half8 k00 = decode8(c0[0], c0[1]);
-    const half8 k01 = decode8(c0[2], c0[3]);
-    const half8 k10 = decode8(c1[0], c1[1]);
-    const half8 k11 = decode8(c1[2], c1[3]);
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const half8 qa = *(const LDS_AS half8*)(qlane + (rb * 8 + 2 * i) * 1024);
-      const half8 qb = *(const LDS_AS half8*)(qlane + (rb * 8 + 2 * i + 1) * 1024);
-      sacc[0][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k00, qa, sacc[0][rb], 0, 0, 0);
-      sacc[1][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k10, qa, sacc[1][rb], 0, 0, 0);
-      sacc[0][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k01, qb, sacc[0][rb], 0, 0, 0);
-      sacc[1][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k11, qb, sacc[1][rb], 0, 0, 0);
-    }
-  }
-  // ---- scores (lane holds keys t0 + 16kb + 4g + r of its row), row max, reference
-  float s[RB][8];
-  bool restart = false;
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) s[rb][k] = sacc[k >> 2][rb][k & 3];
-    if (masked) {
-#pragma unroll
-      for (int k = 0; k < 8; ++k)
-        if (t0 + 16 * (k >> 2) + 4 * g + (k & 3) > limit[rb]) s[rb][k] = kNegInf;
-    }
-    float tmax = fmaxf(fmaxf(fmaxf(s[rb][0], s[rb][1]), fmaxf(s[rb][2], s[rb][3])),
-                       fmaxf(fmaxf(s[rb][4], s[rb][5]), fmaxf(s[rb][6], s[rb][7])));
-    tmax = max_x32(max_x16(tmax));
-    st.m_max[rb] = fmaxf(st.m_max[rb], tmax);
-    if (st.m_ref[rb] == kNegInf) st.m_ref[rb] = tmax;   // first visible keys of the row (or still -inf)
-    restart |= (st.m_max[rb] - st.m_ref[rb]) * c2 > kRestartLog2;   // false while -inf
-  }
-  if (__builtin_amdgcn_ballot_w64(restart)) return true;
-  // ---- P * 2^3 = exp2((s - m_ref) * c2) * 2^3 as FP16 hi + lo; compensated sums.
-  // (s - m_ref) first: exact for keys near the max, so P keeps full relative
-  // precision even when |m_ref * c2| is large.
-  half8 phi[RB], plo[RB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const bool live = st.m_ref[rb] != kNegInf;
-    float psum = 0.f;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const float p = live ? fast_exp2((s[rb][k] - st.m_ref[rb]) * c2) : 0.f;
-      psum += p;
-      const float ph = p * kPScale;
-      phi[rb][k] = (_Float16)ph;
-      plo[rb][k] = (_Float16)(ph - (float)phi[rb][k]);
-    }
-    comp_add(st.l_sum[rb], st.l_cmp[rb], psum);
-  }
-  // ---- O^T += V^T * P^T; lane (n, g) reads 8 keys of dimension 16mb + n.
-  // MFMA K-index 8g + k of this lane holds key 4g + k (k < 4) or 16 + 4g + k - 4,
-  // matching the score layout above.  Keys at or past L hold unrelated bytes;
-  // their codes are cleared to +0 before decode so 0 * NaN never reaches O.
-  const int j = n >> 1;
-  const int vslot = 4 * g + (j & 3);
-  const unsigned vrow = (unsigned)(uintptr_t)(vl + (j >> 2) * kPageBytes + vslot * 256 + 8 * (n & 1));
-  const unsigned vsw = 16u * vslot;
-  unsigned keep_lo = 0xffffffffu, keep_hi = 0xffffffffu;
-  if (masked) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      if (t0 + 4 * g + k >= L) keep_lo &= ~(0xffu << (8 * k));
-      if (t0 + 16 + 4 * g + k >= L) keep_hi &= ~(0xffu << (8 * k));
-    }
-  }
-  int2v vnext = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS int2v*)(uintptr_t)(vrow + vsw));
-#pragma unroll
-  for (int mb = 0; mb < 16; ++mb) {
-    const int2v vr = vnext;
-    if (mb < 15)
-      vnext = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-          (LDS_AS int2v*)(uintptr_t)(vrow + xor_in_loop(vsw, 16u * (mb + 1))));
-    const half8 va = decode8((unsigned)vr[0] & keep_lo, (unsigned)vr[1] & keep_hi);
-    // hi products of every row block first, then lo: dependent MFMAs on one
-    // accumulator are RB instructions apart instead of back to back.
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-      st.o[mb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, phi[rb], st.o[mb][rb], 0, 0, 0);
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-      st.o[mb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, plo[rb], st.o[mb][rb], 0, 0, 0);
-  }
-  return false;
-}
-
-__shared__ __attribute__((aligned(16))) uint8_t g_stage0[kStageArray];
-__shared__ __attribute__((aligned(16))) uint8_t g_stage1[kStageArray];
-__shared__ __attribute__((aligned(16))) uint8_t g_qfrag[(kMaxRows / 16) * 8 * 1024];
-__shared__ float g_meta[kWaves][3][kMaxRows];   // per wave: m_ref, m_max, l of every row
+__shared__ __attribute__((aligned(16))) uint8_t g_ring[kStages * kTileBytes];
+// P operands, double-buffered by tile parity: [ks][rb][hi|lo][lane][8 halves].
+__shared__ __attribute__((aligned(16))) uint8_t g_p[2][2 * kMaxRB * 2 * kPSlot];
+__shared__ float g_meta[2][kWaves][kMaxRows];   // per wave: row max / row sum partials
+__shared__ int g_flag[kWaves];                  // a wave's rows outgrew m_ref somewhere in the chunk
+__shared__ int g_pages[2][kWaves][64];          // block-table windows: wave w's pages of 64 tiles
 
 __device__ __forceinline__ int split_size_of(int L, int ns, int fixed) {
   if (fixed) return fixed;
@@ -303,15 +161,9 @@ __device__ __forceinline__ int split_size_of(int L, int ns, int fixed) {
 
 __device__ __forceinline__ int clamp_len(int L, int nq, int maxL) { return min(max(L, nq), maxL); }
 
-// LDS slot of wave s during the fold (4 slots of RB * 8 KB over the two rings).
-template <int RB>
-__device__ __forceinline__ LDS_AS uint8_t* fold_slot(int s) {
-  return (LDS_AS uint8_t*)(s < 2 ? g_stage0 : g_stage1) + (s & 1) * (RB * 8 * 1024);
-}
-
 // Workgroup w -> (split group, chunk): groups (sequence, split) are dealt to
 // XCDs round robin and the C chunks of a group get workgroup ids
-// 8*(C*(grp/8) + c) + grp%8, all on XCD grp % 8.
+// 8*(C*(grp/8) + c) + grp%8, all on XCD grp % 8 (a locality nicety only).
 template <int RB>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_cache,
@@ -342,163 +194,374 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
   const int Tb = (L + kTile - 1) / kTile;
   const int s_lo = min(jsp * (S / kTile), Tb);
   const int s_hi = min((jsp + 1) * (S / kTile), Tb);
-  const int nt = s_hi - s_lo;
-  const int t_lo = s_lo + (chunk * nt) / C;
-  const int t_hi = s_lo + ((chunk + 1) * nt) / C;
+  const int ns32 = s_hi - s_lo;
+  const int t_lo = s_lo + (chunk * ns32) / C;          // chunk = 32-key tiles [t_lo, t_hi)
+  const int t_hi = s_lo + ((chunk + 1) * ns32) / C;
   const int npages = (L + kPage - 1) / kPage;
+  const int page_lo = 2 * t_lo;
+  const int page_end = min(2 * t_hi, npages);          // pages of the chunk that exist
+  const int key_lo = kTile * t_lo;
+  const int key_end = min(kTile * t_hi, L);            // keys of the chunk
+  const int nu = (t_hi - t_lo + 1) / 2;                // 64-key tiles
   const int32_t* bt = block_table + (size_t)b * a.max_blocks;
 
+  // DMA lane offsets: load qq of a page fills LDS row r = 4qq + lane/16, chunk
+  // position lane%16, with global chunk (lane%16) ^ r of that row.
   unsigned lane_off[4];
 #pragma unroll
   for (int qq = 0; qq < 4; ++qq) {
     const unsigned r = 4 * qq + (lane >> 4);
     lane_off[qq] = r * 256u + 16u * ((unsigned)(lane & 15) ^ r);
   }
-  LDS_AS uint8_t* ring0 = (LDS_AS uint8_t*)g_stage0 + wave * kStageBytes;
-  LDS_AS uint8_t* ring1 = (LDS_AS uint8_t*)g_stage1 + wave * kStageBytes;
-  const int t_first = t_lo + wave;
-  // First tile in flight before anything else.
-  if (t_first < t_hi) {
-    const int p0 = bt[2 * t_first];
-    const int p1 = (2 * t_first + 1 < npages) ? bt[2 * t_first + 1] : p0;
-    issue_tile(k_cache, v_cache, p0, p1, ring0, lane_off);
-  }
+  // Wave w's page of tile u is page_lo + 4u + w; pages past the chunk are skipped.
+  auto tile_valid = [&](int u) { return u < nu && page_lo + 4 * u + wave < page_end; };
+  auto issue_page = [&](int u, int page) {
+    if (!tile_valid(u)) return;
+    LDS_AS uint8_t* st = (LDS_AS uint8_t*)g_ring + (u % kStages) * kTileBytes + wave * kPageBytes;
+    const uint8_t* kp = k_cache + (size_t)page * kPageBytes;
+    const uint8_t* vp = v_cache + (size_t)page * kPageBytes;
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) lds_dma16(kp, lane_off[qq], st + qq * 1024);
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) lds_dma16(vp, lane_off[qq], st + kVOffset + qq * 1024);
+  };
+  // Block-table entries come through LDS windows (one dword per lane, window
+  // k = tiles 64k..64k+63, double-buffered) and then one VGPR, so no scalar
+  // load sits between a tile's turn and its DMA; the block table is never read
+  // any other way.  Lanes past the chunk read a valid entry whose value is
+  // never used.
+  auto load_window = [&](int k) {
+    const int tu = 64 * k + lane;
+    const int e = (tu < nu && page_lo + 4 * tu + wave < page_end) ? page_lo + 4 * tu + wave : page_lo;
+    lds_dma4(bt, (unsigned)e * 4u, (LDS_AS void*)&g_pages[k & 1][wave][0]);
+  };
+  // Tile u's DMA, page id from window (u / 64) held in pg.
+  auto issue_tile = [&](int u, int pg) { issue_page(u, __builtin_amdgcn_readlane(pg, u & 63)); };
+  // This wave's LDS loads still allowed in flight once tile u has landed.
+  auto pending_after = [&](int u) {
+    int p = 0;
+#pragma unroll
+    for (int d = 1; d <= kStages - 2; ++d) p += tile_valid(u + d) ? 8 : 0;
+    return p;
+  };
 
-  // Q of sequence b in LDS in MFMA B-operand order: fragment (rb, m), lane
-  // (n,g) = Q[row 16rb+n][64g + 8m + 0..7], zero for rows past 6q.
-  for (int u = tid; u < RB * 8 * 64; u += kThreads) {
-    const int ul = u & 63, um = (u >> 6) & 7, urb = u >> 9;
-    const int row = 16 * urb + (ul & 15);
-    half8 v = half8{};
-    if (row < ROWS) v = *(const half8*)(q + ((size_t)b * ROWS + row) * kHeadDim + 64 * (ul >> 4) + 8 * um);
-    *(LDS_AS half8*)((LDS_AS uint8_t*)g_qfrag + u * 16) = v;
-  }
-  __syncthreads();
-  const LDS_AS uint8_t* qlane = (const LDS_AS uint8_t*)g_qfrag + lane * 16;
-  int limit[RB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int row = 16 * rb + n;
-    limit[rb] = row < ROWS ? (L - NQ + row / kQHeads) : -1;
-  }
-  const int first_masked = (L - NQ) / kTile;   // tiles from here on hold keys some row must not see
-
-  WaveState<RB> st;
-  state_reset(st);
-  int t = t_first;
-  int stage = 0;
-  while (t < t_hi) {
-    const int tn = t + kWaves;
-    if (tn < t_hi) {
-      const int p0 = bt[2 * tn];
-      const int p1 = (2 * tn + 1 < npages) ? bt[2 * tn + 1] : p0;
-      issue_tile(k_cache, v_cache, p0, p1, stage ? ring0 : ring1, lane_off);
-      wait_vmcnt<16>();
-    } else {
-      wait_vmcnt<0>();
-    }
-    if (compute_tile<RB>(st, qlane, stage ? ring1 : ring0, t * kTile, L, limit, t >= first_masked, c2, n,
-                         g)) {
-      // A row max outgrew its reference: raise every reference to the running
-      // max and redo this wave's tiles.
-      wait_vmcnt<0>();
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        st.m_ref[rb] = st.m_max[rb];
-        st.l_sum[rb] = 0.f;
-        st.l_cmp[rb] = 0.f;
-#pragma unroll
-        for (int mb = 0; mb < 16; ++mb) st.o[mb][rb] = float4v{0.f, 0.f, 0.f, 0.f};
-      }
-      t = t_first;
-      stage = 0;
-      const int p0 = bt[2 * t];
-      const int p1 = (2 * t + 1 < npages) ? bt[2 * t + 1] : p0;
-      issue_tile(k_cache, v_cache, p0, p1, ring0, lane_off);
-      continue;
-    }
-    stage ^= 1;
-    t = tn;
-  }
-
-  // ---- fold the four wave states (reduce-scatter through LDS).  Row sums: the
-  // four lanes of a row hold disjoint key subsets.
-  if (g == 0) {
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      g_meta[wave][0][16 * rb + n] = st.m_ref[rb];
-      g_meta[wave][1][16 * rb + n] = st.m_max[rb];
+  // ---- prologue: Q (MFMA B-operand order) into the last ring stage and the
+  // block-table windows 0 and 1, then the first kStages-1 tiles.  Fragment
+  // f = rb*8 + m, lane (n, g) holds Q[row 16rb+n][64g + 8m + 0..7]; rows past
+  // 6q repeat the last real row.
+  {
+    LDS_AS uint8_t* qs = (LDS_AS uint8_t*)g_ring + (kStages - 1) * kTileBytes;
+    const _Float16* qb = q + (size_t)b * ROWS * kHeadDim;
+    for (int f = wave; f < RB * 8; f += kWaves) {
+      const int row = min(16 * (f >> 3) + n, ROWS - 1);
+      lds_dma16(qb, (unsigned)(row * kHeadDim * 2 + 128 * g + 16 * (f & 7)), qs + f * 1024);
     }
   }
+  if (nu > 0) load_window(0);
+  if (nu > 64) load_window(1);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();   // every wave's Q fragments and page windows have landed
+  int pg = g_pages[0][wave][lane];
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const float l = sum_x32(sum_x16(st.l_sum[rb])) + sum_x32(sum_x16(st.l_cmp[rb]));
-    if (g == 0) g_meta[wave][2][16 * rb + n] = l;
-  }
-  __syncthreads();   // every wave is done with its ring; meta is complete
-  // Merge weights of this lane's rows: M = max over waves of m_max, wave s
-  // contributes with e_s = 2^((m_ref_s - M) * c2).
-  float M[RB], e[kWaves][RB], Lsum[RB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int row = 16 * rb + n;
-    M[rb] = kNegInf;
-#pragma unroll
-    for (int s = 0; s < kWaves; ++s) M[rb] = fmaxf(M[rb], g_meta[s][1][row]);
-    Lsum[rb] = 0.f;
-#pragma unroll
-    for (int s = 0; s < kWaves; ++s) {
-      const float mr = g_meta[s][0][row];
-      e[s][rb] = (mr != kNegInf) ? fast_exp2((mr - M[rb]) * c2) : 0.f;
-      Lsum[rb] += g_meta[s][2][row] * e[s][rb];
-    }
-  }
-  // Two halves of the dimensions; in half h, waves 2h and 2h+1 merge the
-  // quarters 2h and 2h+1 (16-dim blocks mb = 4v .. 4v+3).
-  float4v res[4][RB];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    if (h) __syncthreads();   // readers of the first half are done
-    LDS_AS uint8_t* mine = fold_slot<RB>(wave);
+  for (int u = 0; u < kStages - 1; ++u) issue_tile(u, pg);
+  half8 qf[RB][8];
+  {
+    const LDS_AS uint8_t* qs = (const LDS_AS uint8_t*)g_ring + (kStages - 1) * kTileBytes + lane * 16;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int mbl = 0; mbl < 8; ++mbl)
-        *(LDS_AS float4v*)(mine + ((rb * 8 + mbl) * 64 + lane) * 16) = st.o[8 * h + mbl][rb];
-    __syncthreads();
-    if ((wave >> 1) == h) {
-      const int base = 4 * (wave & 1);
+      for (int m = 0; m < 8; ++m) {
+        qf[rb][m] = *(const LDS_AS half8*)(qs + (rb * 8 + m) * 1024);
+        asm volatile("" : "+a"(qf[rb][m]));   // Q lives in AGPRs: MFMA reads B from there directly
+      }
+  }
+
+  // Causal bound of each of this lane's rows, also cut at the chunk end.
+  int limit[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int row = min(16 * rb + n, ROWS - 1);
+    limit[rb] = min(L - NQ + row / kQHeads, key_end - 1);
+  }
+  const int lim_min = min(L - NQ, key_end - 1);   // tiles past this hold keys some row must not see
+
+  float4v o[4][RB];      // O^T (x 2^3, relative to m_ref): dims 16(4w+mb) + 4g + 0..3 of row 16rb + n
+  float m_ref[RB], m_max[RB], l_sum[RB], l_cmp[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    m_ref[rb] = kNegInf;
+    m_max[rb] = kNegInf;
+    l_sum[rb] = 0.f;
+    l_cmp[rb] = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) o[mb][rb] = float4v{0.f, 0.f, 0.f, 0.f};
+  }
+  bool have_ref = false;
+  bool sticky = false;   // some row of this wave outgrew m_ref during the chunk
+
+  // V operand addresses (ds_read_b64_tr_b8): lane (n, g) reads row (page j/4,
+  // slot 4g + j%4), j = n/2, bytes 8(n%2)..+7 of 16-byte chunk mb; after the
+  // transpose it holds 8 keys of dimension 16mb + n, MFMA K-index 8g + k being
+  // key 4g + k of page 0 (k < 4) or key 4g + k - 4 of page 1.
+  const int vj = n >> 1;
+  const int vslot = 4 * g + (vj & 3);
+  const unsigned vlane = (vj >> 2) * kPageBytes + vslot * 256 + 8 * (n & 1);
+  const unsigned vsw = 16u * vslot;
+
+  auto stage_of = [&](int t) { return (LDS_AS uint8_t*)g_ring + (t % kStages) * kTileBytes; };
+  auto masked_tile = [&](int t) { return key_lo + kTileKeys * t + kTileKeys - 1 > lim_min; };
+
+  // Rows of this wave's V page at or past the chunk end hold unrelated bytes
+  // (or nothing, for a page that was not loaded): clear their codes to +0 so
+  // that P = 0 times V never turns into 0 * NaN.  Only the chunk's last tile.
+  auto clear_tail = [&](int t) {
+    const int r0 = max(0, key_end - kPage * (page_lo + 4 * t + wave));
+    if (r0 >= kPage) return;
+    LDS_AS uint8_t* vp = stage_of(t) + kVOffset + wave * kPageBytes;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int idx = e * 64 + lane;   // 16-byte chunk idx of the page, row idx / 16
+      if ((idx >> 4) >= r0) *(LDS_AS uint4v*)(vp + idx * 16) = uint4v{0u, 0u, 0u, 0u};
+    }
+  };
+
+  // S^T = K_w * Q^T for this wave's page of tile t and every row block; lane
+  // holds keys key_lo + 64t + 16w + 4g + r of row 16rb + n.
+  auto qk = [&](int t, float (&s)[RB][4]) {
+    float4v sacc[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) sacc[rb] = float4v{0.f, 0.f, 0.f, 0.f};
+    const LDS_AS uint8_t* krow = stage_of(t) + wave * kPageBytes + n * 256;
+    uint4v kr = *(const LDS_AS uint4v*)(krow + 16 * ((4 * g) ^ n));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4v cur = kr;
+      if (i < 3) kr = *(const LDS_AS uint4v*)(krow + 16 * ((4 * g + i + 1) ^ n));
+      const half8 k0 = decode8(cur[0], cur[1]);
+      const half8 k1 = decode8(cur[2], cur[3]);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+        sacc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, qf[rb][2 * i], sacc[rb], 0, 0, 0);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+        sacc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, qf[rb][2 * i + 1], sacc[rb], 0, 0, 0);
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s[rb][r] = sacc[rb][r];
+    if (masked_tile(t)) {
+      const int kb = key_lo + kTileKeys * t + 16 * wave + 4 * g;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int k = 0; k < 4; ++k) res[k][rb] = float4v{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < kWaves; ++s) {
-        const LDS_AS uint8_t* src = fold_slot<RB>(s);
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-          for (int k = 0; k < 4; ++k)
-            res[k][rb] += *(const LDS_AS float4v*)(src + ((rb * 8 + base + k) * 64 + lane) * 16) * e[s][rb];
-      }
+        for (int r = 0; r < 4; ++r)
+          if (kb + r > limit[rb]) s[rb][r] = kNegInf;
     }
+  };
+
+  // Row maxima of this wave's keys; running max; overflow test against m_ref.
+  auto row_max = [&](const float (&s)[RB][4], float (&tmax)[RB]) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const float t = fmaxf(fmaxf(s[rb][0], s[rb][1]), fmaxf(s[rb][2], s[rb][3]));
+      tmax[rb] = max_x32(max_x16(t));
+      m_max[rb] = fmaxf(m_max[rb], tmax[rb]);
+    }
+  };
+  auto overflow = [&]() {
+    bool ovf = false;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) ovf |= (m_max[rb] - m_ref[rb]) * c2 > kRestartLog2;   // false while -inf
+    return __builtin_amdgcn_ballot_w64(ovf) != 0;
+  };
+  // P * 2^3 = exp2((s - m_ref) * c2 + 3) of row block rb as FP16 hi + lo;
+  // compensated row sums.  (s - m_ref) first: exact for keys near the max, so P
+  // keeps full relative precision even when |m_ref * c2| is large.
+  auto probs = [&](int rb, const float (&s)[RB][4], half4& hi, half4& lo) {
+    const float mr = (m_ref[rb] == kNegInf) ? 0.f : m_ref[rb];   // a row without keys has s = -inf
+    float psum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float p8 = fast_exp2(__builtin_fmaf(s[rb][r] - mr, c2, kPScaleLog2));
+      psum += p8;
+      hi[r] = (_Float16)p8;
+      lo[r] = (_Float16)(p8 - (float)hi[r]);
+    }
+    comp_add(l_sum[rb], l_cmp[rb], psum);
+  };
+  // Publish P of tile t for the PV step of every wave: operand (ks, rb, hi|lo),
+  // lane (n, g), halves 4(w%2)..+3, ks = w/2.
+  auto store_p = [&](int t, int rb, const half4& hi, const half4& lo) {
+    LDS_AS uint8_t* pw = (LDS_AS uint8_t*)g_p[t & 1] + lane * 16 + 8 * (wave & 1);
+    const int slot = ((wave >> 1) * RB + rb) * 2;
+    *(LDS_AS half4*)(pw + slot * kPSlot) = hi;
+    *(LDS_AS half4*)(pw + (slot + 1) * kPSlot) = lo;
+  };
+
+  // One PV step: 32 keys (pages 2ks, 2ks+1 of tile t), 16 dims (block 4w + mb).
+  auto pv_step = [&](int t, int ks, int mb, const half8 (&phi)[RB], const half8 (&plo)[RB]) {
+    const unsigned vbase = (unsigned)(uintptr_t)(stage_of(t) + kVOffset + 2 * ks * kPageBytes) + vlane;
+    const int2v vr = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+        (LDS_AS int2v*)(uintptr_t)(vbase + xor_in_loop(vsw, 16u * (4 * wave + mb))));
+    const half8 va = decode8((unsigned)vr[0], (unsigned)vr[1]);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+      o[mb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, phi[rb], o[mb][rb], 0, 0, 0);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+      o[mb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, plo[rb], o[mb][rb], 0, 0, 0);
+  };
+  auto load_p = [&](int t, int ks, half8 (&phi)[RB], half8 (&plo)[RB]) {
+    const LDS_AS uint8_t* pr = (const LDS_AS uint8_t*)g_p[t & 1] + lane * 16;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      phi[rb] = *(const LDS_AS half8*)(pr + ((ks * RB + rb) * 2) * kPSlot);
+      plo[rb] = *(const LDS_AS half8*)(pr + ((ks * RB + rb) * 2 + 1) * kPSlot);
+    }
+  };
+
+  // Front half of tile t without overlap (first tile, or after a restart):
+  // scores, reference (first time), probabilities published, barrier.
+  auto front_plain = [&](int t) {
+    wait_dma(pending_after(t));
+    if (key_lo + kTileKeys * (t + 1) > key_end) clear_tail(t);
+    float s[RB][4], tmax[RB];
+    qk(t, s);
+    row_max(s, tmax);
+    if (!have_ref) {
+      // First tile of the chunk: the shared reference is its max over all four pages.
+      if (g == 0) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) g_meta[0][wave][16 * rb + n] = tmax[rb];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const int row = 16 * rb + n;
+        m_ref[rb] = fmaxf(fmaxf(g_meta[0][0][row], g_meta[0][1][row]),
+                          fmaxf(g_meta[0][2][row], g_meta[0][3][row]));
+      }
+      have_ref = true;
+    }
+    sticky |= overflow();
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      half4 hi, lo;
+      probs(rb, s, hi, lo);
+      store_p(t, rb, hi, lo);
+    }
+    __syncthreads();
+  };
+
+  if (nu > 0) front_plain(0);
+  float M[RB], lsum[RB];
+  for (;;) {
+    int u = 0;
+    while (u < nu) {
+      // P(u) of all four pages is in LDS; every wave is past tile u's barrier,
+      // so the stage of tile u-1 is free for tile u+3.
+      const int tn = u + kStages - 1;
+      if (tn < nu) {
+        if ((tn & 63) == 0 && tn > 0) {
+          pg = g_pages[(tn >> 6) & 1][wave][lane];
+          if (tn + 64 < nu) load_window((tn >> 6) + 1);
+        }
+        issue_tile(tn, pg);
+      }
+      half8 phi[RB], plo[RB];
+      load_p(u, 0, phi, plo);
+      if (u + 1 < nu) {
+        // Overlapped: QK^T of tile u+1, then PV of tile u interleaved with the
+        // softmax of tile u+1, which only needs VALU and the permute network.
+        wait_dma(pending_after(u + 1));
+        if (key_lo + kTileKeys * (u + 2) > key_end) clear_tail(u + 1);
+        float s[RB][4], tmax[RB];
+        qk(u + 1, s);
+        pv_step(u, 0, 0, phi, plo);
+        row_max(s, tmax);
+        pv_step(u, 0, 1, phi, plo);
+        sticky |= overflow();
+        half4 hi[RB], lo[RB];
+        probs(0, s, hi[0], lo[0]);
+        pv_step(u, 0, 2, phi, plo);
+        if (RB > 1) probs(1 < RB ? 1 : 0, s, hi[1 < RB ? 1 : 0], lo[1 < RB ? 1 : 0]);
+        pv_step(u, 0, 3, phi, plo);
+        load_p(u, 1, phi, plo);
+        if (RB > 2) probs(2 < RB ? 2 : 0, s, hi[2 < RB ? 2 : 0], lo[2 < RB ? 2 : 0]);
+        pv_step(u, 1, 0, phi, plo);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) store_p(u + 1, rb, hi[rb], lo[rb]);
+        pv_step(u, 1, 1, phi, plo);
+        pv_step(u, 1, 2, phi, plo);
+        pv_step(u, 1, 3, phi, plo);
+        __syncthreads();   // P(u+1) published; every wave is done with tile u
+      } else {
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) pv_step(u, 0, mb, phi, plo);
+        load_p(u, 1, phi, plo);
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) pv_step(u, 1, mb, phi, plo);
+      }
+      ++u;
+    }
+
+    // ---- end of chunk: true row max and sum over the four waves' pages (in
+    // wave order), and whether any wave saw a row outgrow its reference.
+    if (g == 0) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) g_meta[0][wave][16 * rb + n] = m_max[rb];
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const float l = sum_x32(sum_x16(l_sum[rb])) + sum_x32(sum_x16(l_cmp[rb]));
+      if (g == 0) g_meta[1][wave][16 * rb + n] = l;
+    }
+    g_flag[wave] = sticky;
+    __syncthreads();
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int row = 16 * rb + n;
+      M[rb] = fmaxf(fmaxf(g_meta[0][0][row], g_meta[0][1][row]), fmaxf(g_meta[0][2][row], g_meta[0][3][row]));
+      lsum[rb] = ((g_meta[1][0][row] + g_meta[1][1][row]) + g_meta[1][2][row]) + g_meta[1][3][row];
+    }
+    if (!(g_flag[0] | g_flag[1] | g_flag[2] | g_flag[3])) break;
+    // Some row max outgrew its reference (P beyond FP16 range somewhere): take
+    // the chunk's true row max as the reference and redo the chunk.  The
+    // reference now bounds every score, so this happens at most once.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      m_ref[rb] = M[rb];
+      l_sum[rb] = 0.f;
+      l_cmp[rb] = 0.f;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) o[mb][rb] = float4v{0.f, 0.f, 0.f, 0.f};
+    }
+    sticky = false;
+    load_window(0);   // this wave's own window buffers: no other wave reads them
+    if (nu > 64) load_window(1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    pg = g_pages[0][wave][lane];
+#pragma unroll
+    for (int v = 0; v < kStages - 1; ++v) issue_tile(v, pg);
+    front_plain(0);   // its barrier also orders every read of g_meta / g_flag above
   }
-  // Wave v now holds dims 16mb + 4g + 0..3 for mb = 4v..4v+3 of rows 16rb + n.
-  // One chunk per split: the state goes straight to the workspace.  Several:
-  // chunk states go to scratch in the workspace layout with the chunk index
-  // innermost, and the merge kernel reduces them in chunk order.
+
   const size_t row0 = (size_t)b * ROWS;
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const int row = 16 * rb + n;
     if (row < ROWS) {
+      const float e = (m_ref[rb] == kNegInf) ? 0.f : fast_exp2((m_ref[rb] - M[rb]) * c2);
       const size_t idx = ((row0 + row) * NS + jsp) * C + chunk;
+      const float of = e * ofac;
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
-        *(float4v*)(a.st_num + idx * kHeadDim + 16 * (4 * wave + k) + 4 * g) = res[k][rb] * ofac;
+      for (int mb = 0; mb < 4; ++mb)
+        *(float4v*)(a.st_num + idx * kHeadDim + 16 * (4 * wave + mb) + 4 * g) = o[mb][rb] * of;
       if (wave == 0 && g == 0) {
         a.st_max[idx] = (M[rb] == kNegInf) ? kNegInf : M[rb] * c;
-        a.st_sum[idx] = Lsum[rb];
+        a.st_sum[idx] = lsum[rb] * e * (1.0f / kPScale);
       }
     }
   }
