@@ -28,7 +28,9 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0          # MI355X published HBM3E bandwidth
 V100_16LAYER_MS = 12.983        # the pages' 16-layer q8 attention on V100 (context only)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "split_kernel_traffic.json")
-SPLIT_SRC = os.path.join(ROOT, "long_context_split_amd", "csrc", "split_kernel.hip")
+SPLIT_SRCS = [os.path.join(ROOT, "long_context_split_amd", "csrc", "split_kernel.hip"),
+              os.path.join(ROOT, "long_context_split_amd", "csrc", "dfv_common.h"),
+              os.path.join(ROOT, "long_context_split_amd", "build.py")]
 
 
 def parse():
@@ -40,12 +42,18 @@ def parse():
     p.add_argument("--num-q", type=int, default=None)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--graph", action="store_true", help="time a captured HIP graph of the step")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="after timing, run a plain 512 MiB device-to-device copy (reference for HBM counters)")
     return p.parse_args()
 
 
 def src_hash() -> str:
-    with open(SPLIT_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of everything that shapes the split kernel's binary (source, shared header, flags)."""
+    h = hashlib.sha256()
+    for p in SPLIT_SRCS:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(launch_bytes_alg: float):
@@ -193,6 +201,13 @@ def main():
                      "kernel": "split_kernel",
                      "algorithmic_bytes_per_launch": kv_bytes_layer},
     }
+    if args.calibrate_copy:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        line["calibration_copy_bytes"] = 512 << 20
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.workload, nq)
     else:
