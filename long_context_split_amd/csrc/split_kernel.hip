@@ -73,6 +73,7 @@ constexpr int kStages = 4;                   // LDS ring depth
 constexpr int kTileBytes = 8 * kPageBytes;   // K pages 0..3, then V pages 0..3 (32 KB)
 constexpr int kVOffset = 4 * kPageBytes;
 constexpr int kPSlot = 64 * 16;              // one (k-step, row block, hi|lo) P operand: 64 lanes x 16 B
+constexpr int kSplitThreads = 2 * kThreads;  // four score waves + four PV waves, two per SIMD
 
 // Eight E4M3 codes (two dwords) to eight FP16 values, two codes per instruction.
 __device__ __forceinline__ half8 decode8(unsigned lo, unsigned hi) {
@@ -149,7 +150,7 @@ __device__ __forceinline__ void wait_dma(int pending) {
 __shared__ __attribute__((aligned(16))) uint8_t g_ring[kStages * kTileBytes];
 // P operands, double-buffered by tile parity: [ks][rb][hi|lo][lane][8 halves].
 __shared__ __attribute__((aligned(16))) uint8_t g_p[2][2 * kMaxRB * 2 * kPSlot];
-__shared__ float g_meta[2][kWaves][kMaxRows];   // per wave: row max / row sum partials
+__shared__ float g_meta[3][kWaves][kMaxRows];   // per score wave: row max, row sum, reference
 __shared__ int g_flag[kWaves];                  // a wave's rows outgrew m_ref somewhere in the chunk
 __shared__ int g_pages[2][kWaves][64];          // block-table windows: wave w's pages of 64 tiles
 
@@ -164,15 +165,23 @@ __device__ __forceinline__ int clamp_len(int L, int nq, int maxL) { return min(m
 // Workgroup w -> (split group, chunk): groups (sequence, split) are dealt to
 // XCDs round robin and the C chunks of a group get workgroup ids
 // 8*(C*(grp/8) + c) + grp%8, all on XCD grp % 8 (a locality nicety only).
+//
+// Eight waves, two per SIMD, in two roles: waves 0-3 ("score waves") own page
+// w of every tile: its DMAs, QK^T, softmax and the P operands; waves 4-7 ("PV
+// waves") own dimensions 64w..64w+63: V decode and the PV products.  On each
+// SIMD one wave of each kind runs, so the MFMA pipe works on one wave's
+// products while the other wave's VALU work (decode, exp, packing) proceeds.
 template <int RB>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kSplitThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_cache,
                   const uint8_t* __restrict__ v_cache, const int32_t* __restrict__ block_table,
                   const int32_t* __restrict__ context_lens, const float* __restrict__ k_scale,
                   const float* __restrict__ v_scale, SplitArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool scorer = wid < kWaves;
+  const int wave = wid & (kWaves - 1);   // page (score wave) or dimension slice (PV wave)
   const int n = lane & 15;
   const int g = lane >> 4;
   const int NQ = a.num_q;
@@ -205,6 +214,9 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
   const int nu = (t_hi - t_lo + 1) / 2;                // 64-key tiles
   const int32_t* bt = block_table + (size_t)b * a.max_blocks;
 
+  auto stage_of = [&](int t) { return (LDS_AS uint8_t*)g_ring + (t % kStages) * kTileBytes; };
+
+  // ------------------------------------------------------------------ score waves
   // DMA lane offsets: load qq of a page fills LDS row r = 4qq + lane/16, chunk
   // position lane%16, with global chunk (lane%16) ^ r of that row.
   unsigned lane_off[4];
@@ -217,7 +229,7 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
   auto tile_valid = [&](int u) { return u < nu && page_lo + 4 * u + wave < page_end; };
   auto issue_page = [&](int u, int page) {
     if (!tile_valid(u)) return;
-    LDS_AS uint8_t* st = (LDS_AS uint8_t*)g_ring + (u % kStages) * kTileBytes + wave * kPageBytes;
+    LDS_AS uint8_t* st = stage_of(u) + wave * kPageBytes;
     const uint8_t* kp = k_cache + (size_t)page * kPageBytes;
     const uint8_t* vp = v_cache + (size_t)page * kPageBytes;
 #pragma unroll
@@ -235,7 +247,6 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
     const int e = (tu < nu && page_lo + 4 * tu + wave < page_end) ? page_lo + 4 * tu + wave : page_lo;
     lds_dma4(bt, (unsigned)e * 4u, (LDS_AS void*)&g_pages[k & 1][wave][0]);
   };
-  // Tile u's DMA, page id from window (u / 64) held in pg.
   auto issue_tile = [&](int u, int pg) { issue_page(u, __builtin_amdgcn_readlane(pg, u & 63)); };
   // This wave's LDS loads still allowed in flight once tile u has landed.
   auto pending_after = [&](int u) {
@@ -245,38 +256,8 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
     return p;
   };
 
-  // ---- prologue: Q (MFMA B-operand order) into the last ring stage and the
-  // block-table windows 0 and 1, then the first kStages-1 tiles.  Fragment
-  // f = rb*8 + m, lane (n, g) holds Q[row 16rb+n][64g + 8m + 0..7]; rows past
-  // 6q repeat the last real row.
-  {
-    LDS_AS uint8_t* qs = (LDS_AS uint8_t*)g_ring + (kStages - 1) * kTileBytes;
-    const _Float16* qb = q + (size_t)b * ROWS * kHeadDim;
-    for (int f = wave; f < RB * 8; f += kWaves) {
-      const int row = min(16 * (f >> 3) + n, ROWS - 1);
-      lds_dma16(qb, (unsigned)(row * kHeadDim * 2 + 128 * g + 16 * (f & 7)), qs + f * 1024);
-    }
-  }
-  if (nu > 0) load_window(0);
-  if (nu > 64) load_window(1);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();   // every wave's Q fragments and page windows have landed
-  int pg = g_pages[0][wave][lane];
-#pragma unroll
-  for (int u = 0; u < kStages - 1; ++u) issue_tile(u, pg);
-  half8 qf[RB][8];
-  {
-    const LDS_AS uint8_t* qs = (const LDS_AS uint8_t*)g_ring + (kStages - 1) * kTileBytes + lane * 16;
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        qf[rb][m] = *(const LDS_AS half8*)(qs + (rb * 8 + m) * 1024);
-        asm volatile("" : "+a"(qf[rb][m]));   // Q lives in AGPRs: MFMA reads B from there directly
-      }
-  }
-
-  // Causal bound of each of this lane's rows, also cut at the chunk end.
+  // Causal bound of each of this lane's rows (rows past 6q act as the last
+  // real row), also cut at the chunk end.
   int limit[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
@@ -284,31 +265,6 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
     limit[rb] = min(L - NQ + row / kQHeads, key_end - 1);
   }
   const int lim_min = min(L - NQ, key_end - 1);   // tiles past this hold keys some row must not see
-
-  float4v o[4][RB];      // O^T (x 2^3, relative to m_ref): dims 16(4w+mb) + 4g + 0..3 of row 16rb + n
-  float m_ref[RB], m_max[RB], l_sum[RB], l_cmp[RB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    m_ref[rb] = kNegInf;
-    m_max[rb] = kNegInf;
-    l_sum[rb] = 0.f;
-    l_cmp[rb] = 0.f;
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) o[mb][rb] = float4v{0.f, 0.f, 0.f, 0.f};
-  }
-  bool have_ref = false;
-  bool sticky = false;   // some row of this wave outgrew m_ref during the chunk
-
-  // V operand addresses (ds_read_b64_tr_b8): lane (n, g) reads row (page j/4,
-  // slot 4g + j%4), j = n/2, bytes 8(n%2)..+7 of 16-byte chunk mb; after the
-  // transpose it holds 8 keys of dimension 16mb + n, MFMA K-index 8g + k being
-  // key 4g + k of page 0 (k < 4) or key 4g + k - 4 of page 1.
-  const int vj = n >> 1;
-  const int vslot = 4 * g + (vj & 3);
-  const unsigned vlane = (vj >> 2) * kPageBytes + vslot * 256 + 8 * (n & 1);
-  const unsigned vsw = 16u * vslot;
-
-  auto stage_of = [&](int t) { return (LDS_AS uint8_t*)g_ring + (t % kStages) * kTileBytes; };
   auto masked_tile = [&](int t) { return key_lo + kTileKeys * t + kTileKeys - 1 > lim_min; };
 
   // Rows of this wave's V page at or past the chunk end hold unrelated bytes
@@ -325,18 +281,30 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
     }
   };
 
-  // S^T = K_w * Q^T for this wave's page of tile t and every row block; lane
-  // holds keys key_lo + 64t + 16w + 4g + r of row 16rb + n.
+  half8 qf[RB][8];       // Q in MFMA B-operand order (score waves; AGPRs)
+  float m_ref[RB], m_lane[RB], l_sum[RB], l_cmp[RB];
+  int pg = 0;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    m_ref[rb] = kNegInf;
+    m_lane[rb] = kNegInf;
+    l_sum[rb] = 0.f;
+    l_cmp[rb] = 0.f;
+  }
+  const unsigned kswz = 16u * (unsigned)n;   // K row n, chunk (4g+i)^n, as n*256 + 16*((4g+i)^n)
+
+  // S^T = K_w * Q^T for this wave's page of tile t; lane holds keys
+  // key_lo + 64t + 16w + 4g + r of row 16rb + n.  Masked keys get -inf.
   auto qk = [&](int t, float (&s)[RB][4]) {
     float4v sacc[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) sacc[rb] = float4v{0.f, 0.f, 0.f, 0.f};
     const LDS_AS uint8_t* krow = stage_of(t) + wave * kPageBytes + n * 256;
-    uint4v kr = *(const LDS_AS uint4v*)(krow + 16 * ((4 * g) ^ n));
+    uint4v kr = *(const LDS_AS uint4v*)(krow + ((16u * (4 * g)) ^ kswz));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint4v cur = kr;
-      if (i < 3) kr = *(const LDS_AS uint4v*)(krow + 16 * ((4 * g + i + 1) ^ n));
+      if (i < 3) kr = *(const LDS_AS uint4v*)(krow + ((16u * (4 * g + i + 1)) ^ kswz));
       const half8 k0 = decode8(cur[0], cur[1]);
       const half8 k1 = decode8(cur[2], cur[3]);
 #pragma unroll
@@ -359,81 +327,153 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
           if (kb + r > limit[rb]) s[rb][r] = kNegInf;
     }
   };
-
-  // Row maxima of this wave's keys; running max; overflow test against m_ref.
-  auto row_max = [&](const float (&s)[RB][4], float (&tmax)[RB]) {
+  // Running max of this lane's keys (cross-lane reduction only at the chunk end).
+  auto lane_max = [&](const float (&s)[RB][4]) {
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const float t = fmaxf(fmaxf(s[rb][0], s[rb][1]), fmaxf(s[rb][2], s[rb][3]));
-      tmax[rb] = max_x32(max_x16(t));
-      m_max[rb] = fmaxf(m_max[rb], tmax[rb]);
-    }
+    for (int rb = 0; rb < RB; ++rb)
+      m_lane[rb] = fmaxf(fmaxf(m_lane[rb], fmaxf(s[rb][0], s[rb][1])), fmaxf(s[rb][2], s[rb][3]));
   };
-  auto overflow = [&]() {
-    bool ovf = false;
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) ovf |= (m_max[rb] - m_ref[rb]) * c2 > kRestartLog2;   // false while -inf
-    return __builtin_amdgcn_ballot_w64(ovf) != 0;
-  };
-  // P * 2^3 = exp2((s - m_ref) * c2 + 3) of row block rb as FP16 hi + lo;
-  // compensated row sums.  (s - m_ref) first: exact for keys near the max, so P
-  // keeps full relative precision even when |m_ref * c2| is large.
-  auto probs = [&](int rb, const float (&s)[RB][4], half4& hi, half4& lo) {
-    const float mr = (m_ref[rb] == kNegInf) ? 0.f : m_ref[rb];   // a row without keys has s = -inf
-    float psum = 0.f;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float p8 = fast_exp2(__builtin_fmaf(s[rb][r] - mr, c2, kPScaleLog2));
-      psum += p8;
-      hi[r] = (_Float16)p8;
-      lo[r] = (_Float16)(p8 - (float)hi[r]);
-    }
-    comp_add(l_sum[rb], l_cmp[rb], psum);
-  };
-  // Publish P of tile t for the PV step of every wave: operand (ks, rb, hi|lo),
-  // lane (n, g), halves 4(w%2)..+3, ks = w/2.
-  auto store_p = [&](int t, int rb, const half4& hi, const half4& lo) {
+  // P * 2^3 = exp2((s - m_ref) * c2 + 3) as FP16 hi (truncated) + FP16 lo (the
+  // exact remainder, rounded); compensated row sums.  (s - m_ref) first: exact
+  // for keys near the max, so P keeps full relative precision even when
+  // |m_ref * c2| is large.  Published for every PV wave: operand (ks, rb,
+  // hi|lo), lane (n, g), halves 4(w%2)..+3, ks = w/2.
+  auto publish_p = [&](int t, const float (&s)[RB][4]) {
     LDS_AS uint8_t* pw = (LDS_AS uint8_t*)g_p[t & 1] + lane * 16 + 8 * (wave & 1);
-    const int slot = ((wave >> 1) * RB + rb) * 2;
-    *(LDS_AS half4*)(pw + slot * kPSlot) = hi;
-    *(LDS_AS half4*)(pw + (slot + 1) * kPSlot) = lo;
-  };
-
-  // One PV step: 32 keys (pages 2ks, 2ks+1 of tile t), 16 dims (block 4w + mb).
-  auto pv_step = [&](int t, int ks, int mb, const half8 (&phi)[RB], const half8 (&plo)[RB]) {
-    const unsigned vbase = (unsigned)(uintptr_t)(stage_of(t) + kVOffset + 2 * ks * kPageBytes) + vlane;
-    const int2v vr = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-        (LDS_AS int2v*)(uintptr_t)(vbase + xor_in_loop(vsw, 16u * (4 * wave + mb))));
-    const half8 va = decode8((unsigned)vr[0], (unsigned)vr[1]);
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-      o[mb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, phi[rb], o[mb][rb], 0, 0, 0);
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-      o[mb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, plo[rb], o[mb][rb], 0, 0, 0);
-  };
-  auto load_p = [&](int t, int ks, half8 (&phi)[RB], half8 (&plo)[RB]) {
-    const LDS_AS uint8_t* pr = (const LDS_AS uint8_t*)g_p[t & 1] + lane * 16;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      phi[rb] = *(const LDS_AS half8*)(pr + ((ks * RB + rb) * 2) * kPSlot);
-      plo[rb] = *(const LDS_AS half8*)(pr + ((ks * RB + rb) * 2 + 1) * kPSlot);
+      const float mr = (m_ref[rb] == kNegInf) ? 0.f : m_ref[rb];   // a row without keys has s = -inf
+      float p8[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) p8[r] = fast_exp2(__builtin_fmaf(s[rb][r] - mr, c2, kPScaleLog2));
+      const half2v h01 = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(p8[0], p8[1]));
+      const half2v h23 = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(p8[2], p8[3]));
+      const half4 hi = half4{h01[0], h01[1], h23[0], h23[1]};
+      half4 lo;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) lo[r] = (_Float16)__builtin_fmaf((float)hi[r], -1.0f, p8[r]);
+      comp_add(l_sum[rb], l_cmp[rb], (p8[0] + p8[1]) + (p8[2] + p8[3]));
+      const int slot = ((wave >> 1) * RB + rb) * 2;
+      *(LDS_AS half4*)(pw + slot * kPSlot) = hi;
+      *(LDS_AS half4*)(pw + (slot + 1) * kPSlot) = lo;
     }
   };
-
-  // Front half of tile t without overlap (first tile, or after a restart):
-  // scores, reference (first time), probabilities published, barrier.
-  auto front_plain = [&](int t) {
+  // Scores of tile t up to (not including) publishing: wait, tail, QK, maxima.
+  auto front = [&](int t, float (&s)[RB][4]) {
     wait_dma(pending_after(t));
     if (key_lo + kTileKeys * (t + 1) > key_end) clear_tail(t);
-    float s[RB][4], tmax[RB];
     qk(t, s);
-    row_max(s, tmax);
-    if (!have_ref) {
-      // First tile of the chunk: the shared reference is its max over all four pages.
-      if (g == 0) {
+    lane_max(s);
+  };
+
+  // ------------------------------------------------------------------ PV waves
+  float4v o[4][RB];      // O^T (x 2^3, relative to m_ref): dims 16(4w+mb) + 4g + 0..3 of row 16rb + n
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) g_meta[0][wave][16 * rb + n] = tmax[rb];
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) o[mb][rb] = float4v{0.f, 0.f, 0.f, 0.f};
+  // V operand addresses (ds_read_b64_tr_b8): lane (n, g) reads row (page j/4,
+  // slot 4g + j%4), j = n/2, bytes 8(n%2)..+7 of 16-byte chunk mb; after the
+  // transpose it holds 8 keys of dimension 16mb + n, MFMA K-index 8g + k being
+  // key 4g + k of page 0 (k < 4) or key 4g + k - 4 of page 1.
+  unsigned voff[4];
+  {
+    const int vj = n >> 1;
+    const int vslot = 4 * g + (vj & 3);
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+      voff[mb] = kVOffset + (vj >> 2) * kPageBytes + vslot * 256 + 8 * (n & 1) +
+                 ((16u * (4 * wave + mb)) ^ (16u * vslot));
+  }
+  // PV of tile t: 64 keys as two 32-key MFMA steps (pages 2ks, 2ks+1), for
+  // this wave's four 16-dimension blocks; hi products of every row block first,
+  // then lo, so dependent MFMAs on one accumulator are RB instructions apart.
+  auto pv = [&](int t) {
+    const unsigned sbase = (unsigned)(uintptr_t)stage_of(t);
+    const LDS_AS uint8_t* pr = (const LDS_AS uint8_t*)g_p[t & 1] + lane * 16;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      half8 phi[RB], plo[RB];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        phi[rb] = *(const LDS_AS half8*)(pr + ((ks * RB + rb) * 2) * kPSlot);
+        plo[rb] = *(const LDS_AS half8*)(pr + ((ks * RB + rb) * 2 + 1) * kPSlot);
+      }
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const int2v vr = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (LDS_AS int2v*)(uintptr_t)(sbase + ks * 2 * kPageBytes + voff[mb]));
+        const half8 va = decode8((unsigned)vr[0], (unsigned)vr[1]);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          o[mb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, phi[rb], o[mb][rb], 0, 0, 0);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          o[mb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, plo[rb], o[mb][rb], 0, 0, 0);
+      }
+    }
+  };
+
+  // ------------------------------------------------------------------ prologue
+  // Score waves: Q (MFMA B-operand order) into the last ring stage and the
+  // block-table windows 0 and 1, then the first kStages-1 tiles.  Fragment
+  // f = rb*8 + m, lane (n, g) holds Q[row 16rb+n][64g + 8m + 0..7]; rows past
+  // 6q repeat the last real row.
+  if (scorer) {
+    LDS_AS uint8_t* qs = stage_of(kStages - 1);
+    const _Float16* qb = q + (size_t)b * ROWS * kHeadDim;
+    for (int f = wave; f < RB * 8; f += kWaves) {
+      const int row = min(16 * (f >> 3) + n, ROWS - 1);
+      lds_dma16(qb, (unsigned)(row * kHeadDim * 2 + 128 * g + 16 * (f & 7)), qs + f * 1024);
+    }
+    if (nu > 0) load_window(0);
+    if (nu > 64) load_window(1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  __syncthreads();   // every score wave's Q fragments and page windows have landed
+  if (scorer) {
+    pg = g_pages[0][wave][lane];
+#pragma unroll
+    for (int u = 0; u < kStages - 1; ++u) issue_tile(u, pg);
+    const LDS_AS uint8_t* qs = stage_of(kStages - 1) + lane * 16;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        qf[rb][m] = *(const LDS_AS half8*)(qs + (rb * 8 + m) * 1024);
+        asm volatile("" : "+a"(qf[rb][m]));   // Q lives in AGPRs: MFMA reads B from there directly
+      }
+  }
+  const size_t row0 = (size_t)b * ROWS;
+  float M[RB], lsum[RB], mref_all[RB];
+  // Row max, sum and reference of the chunk, shared by the score waves through
+  // LDS at the end of a pass (after the barrier that follows the writes).
+  auto read_meta = [&]() {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int row = 16 * rb + n;
+      M[rb] = fmaxf(fmaxf(g_meta[0][0][row], g_meta[0][1][row]), fmaxf(g_meta[0][2][row], g_meta[0][3][row]));
+      lsum[rb] = ((g_meta[1][0][row] + g_meta[1][1][row]) + g_meta[1][2][row]) + g_meta[1][3][row];
+      mref_all[rb] = g_meta[2][0][row];
+    }
+    return (g_flag[0] | g_flag[1] | g_flag[2] | g_flag[3]) != 0;
+  };
+
+  // The two roles run separate loops with the same barrier sequence:
+  //   nu > 0: first-tile max exchange, P(0) published;
+  //   per tile u: one barrier (P(u+1) published, PV(u) done);
+  //   end of pass: one barrier (meta written); on a restart one more (P(0)).
+  if (scorer) {
+    // First tile: the shared reference m_ref is its row max over all four pages
+    // (every row that sees any key of the chunk sees its first key).
+    if (nu > 0) {
+      float s[RB][4];
+      front(0, s);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const float t = fmaxf(fmaxf(s[rb][0], s[rb][1]), fmaxf(s[rb][2], s[rb][3]));
+        const float tm = max_x32(max_x16(t));
+        if (g == 0) g_meta[0][wave][16 * rb + n] = tm;
       }
       __syncthreads();
 #pragma unroll
@@ -442,126 +482,106 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
         m_ref[rb] = fmaxf(fmaxf(g_meta[0][0][row], g_meta[0][1][row]),
                           fmaxf(g_meta[0][2][row], g_meta[0][3][row]));
       }
-      have_ref = true;
+      publish_p(0, s);
+      __syncthreads();   // P(0) published
     }
-    sticky |= overflow();
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      half4 hi, lo;
-      probs(rb, s, hi, lo);
-      store_p(t, rb, hi, lo);
-    }
-    __syncthreads();
-  };
-
-  if (nu > 0) front_plain(0);
-  float M[RB], lsum[RB];
-  for (;;) {
-    int u = 0;
-    while (u < nu) {
-      // P(u) of all four pages is in LDS; every wave is past tile u's barrier,
-      // so the stage of tile u-1 is free for tile u+3.
-      const int tn = u + kStages - 1;
-      if (tn < nu) {
-        if ((tn & 63) == 0 && tn > 0) {
-          pg = g_pages[(tn >> 6) & 1][wave][lane];
-          if (tn + 64 < nu) load_window((tn >> 6) + 1);
+    for (;;) {
+      for (int u = 0; u < nu; ++u) {
+        // Every wave is past tile u's barrier: the stage of tile u-1 is free.
+        const int tn = u + kStages - 1;
+        if (tn < nu) {
+          if ((tn & 63) == 0) {
+            pg = g_pages[(tn >> 6) & 1][wave][lane];
+            if (tn + 64 < nu) load_window((tn >> 6) + 1);
+          }
+          issue_tile(tn, pg);
         }
-        issue_tile(tn, pg);
+        if (u + 1 < nu) {
+          float s[RB][4];
+          front(u + 1, s);
+          publish_p(u + 1, s);
+        }
+        __syncthreads();   // P(u+1) published; PV(u) done, so tile u's stage may be refilled
       }
-      half8 phi[RB], plo[RB];
-      load_p(u, 0, phi, plo);
-      if (u + 1 < nu) {
-        // Overlapped: QK^T of tile u+1, then PV of tile u interleaved with the
-        // softmax of tile u+1, which only needs VALU and the permute network.
-        wait_dma(pending_after(u + 1));
-        if (key_lo + kTileKeys * (u + 2) > key_end) clear_tail(u + 1);
-        float s[RB][4], tmax[RB];
-        qk(u + 1, s);
-        pv_step(u, 0, 0, phi, plo);
-        row_max(s, tmax);
-        pv_step(u, 0, 1, phi, plo);
-        sticky |= overflow();
-        half4 hi[RB], lo[RB];
-        probs(0, s, hi[0], lo[0]);
-        pv_step(u, 0, 2, phi, plo);
-        if (RB > 1) probs(1 < RB ? 1 : 0, s, hi[1 < RB ? 1 : 0], lo[1 < RB ? 1 : 0]);
-        pv_step(u, 0, 3, phi, plo);
-        load_p(u, 1, phi, plo);
-        if (RB > 2) probs(2 < RB ? 2 : 0, s, hi[2 < RB ? 2 : 0], lo[2 < RB ? 2 : 0]);
-        pv_step(u, 1, 0, phi, plo);
+      // End of pass: true row max and sum over the four pages (in wave order),
+      // the reference, and whether a row outgrew it.
+      bool ovf = false;
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) store_p(u + 1, rb, hi[rb], lo[rb]);
-        pv_step(u, 1, 1, phi, plo);
-        pv_step(u, 1, 2, phi, plo);
-        pv_step(u, 1, 3, phi, plo);
-        __syncthreads();   // P(u+1) published; every wave is done with tile u
-      } else {
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb) pv_step(u, 0, mb, phi, plo);
-        load_p(u, 1, phi, plo);
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb) pv_step(u, 1, mb, phi, plo);
+      for (int rb = 0; rb < RB; ++rb) {
+        ovf |= (m_lane[rb] - m_ref[rb]) * c2 > kRestartLog2;   // false while -inf
+        const float mx = max_x32(max_x16(m_lane[rb]));
+        const float l = sum_x32(sum_x16(l_sum[rb])) + sum_x32(sum_x16(l_cmp[rb]));
+        if (g == 0) {
+          g_meta[0][wave][16 * rb + n] = mx;
+          g_meta[1][wave][16 * rb + n] = l;
+          g_meta[2][wave][16 * rb + n] = m_ref[rb];
+        }
       }
-      ++u;
-    }
-
-    // ---- end of chunk: true row max and sum over the four waves' pages (in
-    // wave order), and whether any wave saw a row outgrow its reference.
-    if (g == 0) {
+      g_flag[wave] = __builtin_amdgcn_ballot_w64(ovf) != 0;
+      __syncthreads();
+      if (!read_meta()) break;
+      // Some row max outgrew its reference (P beyond FP16 range somewhere):
+      // take the chunk's true row max as the reference and redo the chunk.
+      // The reference now bounds every score, so this happens at most once.
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) g_meta[0][wave][16 * rb + n] = m_max[rb];
-    }
+      for (int rb = 0; rb < RB; ++rb) {
+        m_ref[rb] = M[rb];
+        l_sum[rb] = 0.f;
+        l_cmp[rb] = 0.f;
+      }
+      load_window(0);   // this wave's own window buffers: no other wave reads them
+      if (nu > 64) load_window(1);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      pg = g_pages[0][wave][lane];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const float l = sum_x32(sum_x16(l_sum[rb])) + sum_x32(sum_x16(l_cmp[rb]));
-      if (g == 0) g_meta[1][wave][16 * rb + n] = l;
+      for (int v = 0; v < kStages - 1; ++v) issue_tile(v, pg);
+      float s[RB][4];
+      front(0, s);
+      publish_p(0, s);
+      __syncthreads();   // P(0) published; every read of g_meta / g_flag above is done
     }
-    g_flag[wave] = sticky;
-    __syncthreads();
+    if (wave == 0 && g == 0) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const int row = 16 * rb + n;
+        if (row < ROWS) {
+          const float e = (mref_all[rb] == kNegInf) ? 0.f : fast_exp2((mref_all[rb] - M[rb]) * c2);
+          const size_t idx = ((row0 + row) * NS + jsp) * C + chunk;
+          a.st_max[idx] = (M[rb] == kNegInf) ? kNegInf : M[rb] * c;
+          a.st_sum[idx] = lsum[rb] * e * (1.0f / kPScale);
+        }
+      }
+    }
+  } else {
+    if (nu > 0) {
+      __syncthreads();   // first-tile max exchange
+      __syncthreads();   // P(0) published
+    }
+    for (;;) {
+      for (int u = 0; u < nu; ++u) {
+        pv(u);
+        __syncthreads();   // P(u+1) published; PV(u) done
+      }
+      __syncthreads();   // end-of-pass meta written
+      if (!read_meta()) break;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) o[mb][rb] = float4v{0.f, 0.f, 0.f, 0.f};
+      __syncthreads();   // restart: P(0) published
+    }
+    // Renormalise to the true row max and store this wave's dimensions.
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const int row = 16 * rb + n;
-      M[rb] = fmaxf(fmaxf(g_meta[0][0][row], g_meta[0][1][row]), fmaxf(g_meta[0][2][row], g_meta[0][3][row]));
-      lsum[rb] = ((g_meta[1][0][row] + g_meta[1][1][row]) + g_meta[1][2][row]) + g_meta[1][3][row];
-    }
-    if (!(g_flag[0] | g_flag[1] | g_flag[2] | g_flag[3])) break;
-    // Some row max outgrew its reference (P beyond FP16 range somewhere): take
-    // the chunk's true row max as the reference and redo the chunk.  The
-    // reference now bounds every score, so this happens at most once.
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if (row < ROWS) {
+        const float e = (mref_all[rb] == kNegInf) ? 0.f : fast_exp2((mref_all[rb] - M[rb]) * c2);
+        const size_t idx = ((row0 + row) * NS + jsp) * C + chunk;
+        const float of = e * ofac;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      m_ref[rb] = M[rb];
-      l_sum[rb] = 0.f;
-      l_cmp[rb] = 0.f;
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) o[mb][rb] = float4v{0.f, 0.f, 0.f, 0.f};
-    }
-    sticky = false;
-    load_window(0);   // this wave's own window buffers: no other wave reads them
-    if (nu > 64) load_window(1);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    pg = g_pages[0][wave][lane];
-#pragma unroll
-    for (int v = 0; v < kStages - 1; ++v) issue_tile(v, pg);
-    front_plain(0);   // its barrier also orders every read of g_meta / g_flag above
-  }
-
-  const size_t row0 = (size_t)b * ROWS;
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int row = 16 * rb + n;
-    if (row < ROWS) {
-      const float e = (m_ref[rb] == kNegInf) ? 0.f : fast_exp2((m_ref[rb] - M[rb]) * c2);
-      const size_t idx = ((row0 + row) * NS + jsp) * C + chunk;
-      const float of = e * ofac;
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-        *(float4v*)(a.st_num + idx * kHeadDim + 16 * (4 * wave + mb) + 4 * g) = o[mb][rb] * of;
-      if (wave == 0 && g == 0) {
-        a.st_max[idx] = (M[rb] == kNegInf) ? kNegInf : M[rb] * c;
-        a.st_sum[idx] = lsum[rb] * e * (1.0f / kPScale);
+        for (int mb = 0; mb < 4; ++mb)
+          *(float4v*)(a.st_num + idx * kHeadDim + 16 * (4 * wave + mb) + 4 * g) = o[mb][rb] * of;
       }
     }
   }
@@ -581,7 +601,7 @@ int split_grid(int batch, int num_q, int num_splits) {
 
 hipError_t launch_split(const SplitArgs& a, hipStream_t stream) {
   const int rb = (a.num_q * kQHeads + 15) / 16;
-  const dim3 grid(split_grid(a.batch, a.num_q, a.num_splits)), block(kThreads);
+  const dim3 grid(split_grid(a.batch, a.num_q, a.num_splits)), block(kSplitThreads);
   switch (rb) {
     case 1: hipLaunchKernelGGL(split_kernel<1>, grid, block, 0, stream, a.q, a.k_cache, a.v_cache,
                                a.block_table, a.context_lens, a.k_scale, a.v_scale, a); break;
