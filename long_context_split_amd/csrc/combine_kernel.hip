@@ -21,6 +21,7 @@
 // splits j = v, v+8, ... with each lane owning one dimension and all loads of a
 // batch issued before use; the eight partial sums are added in wave order
 // through LDS.  Every sum has a fixed order, so results are byte-deterministic.
+// Workspace stores are non-temporal: nothing in the launch reads them back.
 #include "dfv_common.h"
 
 namespace dfv {
@@ -88,10 +89,10 @@ __global__ __launch_bounds__(kCombineWaves * 64) void combine_kernel(CombineArgs
         }
         if (j < NS) {
           const size_t w = (size_t)row * NS + j;
-          a.ws_num[w * kHeadDim + 64 * quarter + lane] = oj;
+          __builtin_nontemporal_store(oj, a.ws_num + w * kHeadDim + 64 * quarter + lane);
           if (quarter == 0 && lane == 0) {
-            a.ws_max[w] = mj;
-            a.ws_sum[w] = lj;
+            __builtin_nontemporal_store(mj, a.ws_max + w);
+            __builtin_nontemporal_store(lj, a.ws_sum + w);
           }
         }
       }

@@ -20,21 +20,24 @@
 //     of a split in chunk order, so results are deterministic.
 //   * A workgroup walks its chunk in 64-key tiles, four 16-token pages, through
 //     a four-stage LDS ring fed by 16-byte direct-to-LDS loads
-//     (global_load_lds_dwordx4); three tiles are in flight while one is
-//     computed.  Inside a 256-byte token row the 16-byte chunks are
-//     XOR-swizzled by the row's page slot so operand reads are conflict free.
-//   * The four waves (one per SIMD) split each tile by role.  For QK^T wave w
-//     takes page w: S^T = K_w * Q^T on v_mfma_f32_16x16x32_f16 for all 6q rows
+//     (global_load_lds_dwordx4); the first four tiles go out as soon as the
+//     block table has arrived, and afterwards two tiles are in flight while
+//     one is scored and one is multiplied into V.  Inside a 256-byte token row
+//     the 16-byte chunks are XOR-swizzled by the row's page slot so operand
+//     reads are conflict free.
+//   * Eight waves, two per SIMD, split each tile by role.  For QK^T score wave
+//     w takes page w: S^T = K_w * Q^T on v_mfma_f32_16x16x32_f16 for all 6q rows
 //     (up to three 16-row blocks, Q held in registers), so every K byte is
 //     decoded once and each decoded K fragment feeds every row block (the
 //     pages' reuse of one K fragment across three M16 products, [#589]
 //     Purpose).  Each wave turns its scores into P = exp(s - m_ref) * 2^3 as
 //     FP16 hi + FP16 lo (the pages' probability residual products, ~22 bits)
-//     and publishes them in LDS; after one barrier per tile, wave w forms
+//     and publishes them in LDS; after one barrier per tile, PV wave w forms
 //     O^T += V^T * P^T for its own 64 of the 256 dimensions over all 64 keys,
 //     with the V operand read straight out of LDS by the transposing
 //     ds_read_b64_tr_b8.  No wave ever holds another wave's dimensions, so
-//     there is nothing to fold at the end.
+//     there is nothing to fold at the end.  The chunk state leaves through LDS
+//     as whole 1 KB numerator rows, with non-temporal stores.
 //   * m_ref is a per-row reference max shared by the four waves: the max of
 //     the chunk's first tile (every row that sees any key of the chunk sees
 //     its first key).  Accumulators are never rescaled in the tile loop.
@@ -74,6 +77,7 @@ constexpr int kTileBytes = 8 * kPageBytes;   // K pages 0..3, then V pages 0..3 
 constexpr int kVOffset = 4 * kPageBytes;
 constexpr int kPSlot = 64 * 16;              // one (k-step, row block, hi|lo) P operand: 64 lanes x 16 B
 constexpr int kSplitThreads = 2 * kThreads;  // four score waves + four PV waves, two per SIMD
+constexpr int kORowBytes = 4 * kHeadDim + 16;  // numerator row staged in LDS; the pad spreads 16 rows over all banks
 
 // Eight E4M3 codes (two dwords) to eight FP16 values, two codes per instruction.
 __device__ __forceinline__ half8 decode8(unsigned lo, unsigned hi) {
@@ -140,9 +144,10 @@ __device__ __forceinline__ unsigned xor_in_loop(unsigned a, unsigned k) {
   return r;
 }
 
-// Wait until at most `pending` (0, 8 or 16) of this wave's LDS loads are in flight.
+// Wait until at most `pending` (0, 8, 16 or 24) of this wave's LDS loads are in flight.
 __device__ __forceinline__ void wait_dma(int pending) {
-  if (pending >= 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  if (pending >= 24) asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+  else if (pending >= 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
   else if (pending >= 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
   else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
@@ -167,10 +172,12 @@ __device__ __forceinline__ int clamp_len(int L, int nq, int maxL) { return min(m
 // 8*(C*(grp/8) + c) + grp%8, all on XCD grp % 8 (a locality nicety only).
 //
 // Eight waves, two per SIMD, in two roles: waves 0-3 ("score waves") own page
-// w of every tile: its DMAs, QK^T, softmax and the P operands; waves 4-7 ("PV
-// waves") own dimensions 64w..64w+63: V decode and the PV products.  On each
-// SIMD one wave of each kind runs, so the MFMA pipe works on one wave's
-// products while the other wave's VALU work (decode, exp, packing) proceeds.
+// w of every tile for QK^T, softmax and the P operands; waves 4-7 ("PV
+// waves") own dimensions 64w..64w+63 (V decode and the PV products) and the
+// DMA stream of page w (block-table windows, the tile loads and the waits
+// that precede each hand-over barrier).  On each SIMD one wave of each kind
+// runs, so the MFMA pipe works on one wave's products while the other wave's
+// VALU work (decode, exp, packing) proceeds.
 template <int RB>
 __global__ __launch_bounds__(kSplitThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_cache,
@@ -248,11 +255,12 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
     lds_dma4(bt, (unsigned)e * 4u, (LDS_AS void*)&g_pages[k & 1][wave][0]);
   };
   auto issue_tile = [&](int u, int pg) { issue_page(u, __builtin_amdgcn_readlane(pg, u & 63)); };
-  // This wave's LDS loads still allowed in flight once tile u has landed.
-  auto pending_after = [&](int u) {
+  // This wave's LDS loads still allowed in flight once tile u has landed, when
+  // tiles u+1..u+ahead have been issued after it.
+  auto pending_after = [&](int u, int ahead) {
     int p = 0;
 #pragma unroll
-    for (int d = 1; d <= kStages - 2; ++d) p += tile_valid(u + d) ? 8 : 0;
+    for (int d = 1; d <= kStages - 1; ++d) p += (d <= ahead && tile_valid(u + d)) ? 8 : 0;
     return p;
   };
 
@@ -358,9 +366,9 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
       *(LDS_AS half4*)(pw + (slot + 1) * kPSlot) = lo;
     }
   };
-  // Scores of tile t up to (not including) publishing: wait, tail, QK, maxima.
+  // Scores of tile t up to (not including) publishing: tail, QK, maxima.  The
+  // PV waves have waited for the tile's DMAs before the barrier that precedes.
   auto front = [&](int t, float (&s)[RB][4]) {
-    wait_dma(pending_after(t));
     if (key_lo + kTileKeys * (t + 1) > key_end) clear_tail(t);
     qk(t, s);
     lane_max(s);
@@ -415,27 +423,39 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
   };
 
   // ------------------------------------------------------------------ prologue
-  // Score waves: Q (MFMA B-operand order) into the last ring stage and the
-  // block-table windows 0 and 1, then the first kStages-1 tiles.  Fragment
-  // f = rb*8 + m, lane (n, g) holds Q[row 16rb+n][64g + 8m + 0..7]; rows past
-  // 6q repeat the last real row.
-  if (scorer) {
-    LDS_AS uint8_t* qs = stage_of(kStages - 1);
-    const _Float16* qb = q + (size_t)b * ROWS * kHeadDim;
-    for (int f = wave; f < RB * 8; f += kWaves) {
-      const int row = min(16 * (f >> 3) + n, ROWS - 1);
-      lds_dma16(qb, (unsigned)(row * kHeadDim * 2 + 128 * g + 16 * (f & 7)), qs + f * 1024);
-    }
+  // The PV waves own the DMA stream: PV wave w fetches the block-table windows
+  // of page w (0 and 1) and, as soon as those land, puts page w of the first
+  // kStages tiles in flight (the ring is empty, so every stage is free); it
+  // later waits for each tile before the barrier that hands the tile to the
+  // score waves.  Meanwhile the score waves stage Q, in MFMA B-operand order,
+  // in the P buffers, which nothing else uses before P(0) is published.
+  // Fragment f = rb*8 + m, lane (n, g) holds Q[row 16rb+n][64g + 8m + 0..7];
+  // rows past 6q repeat the last real row.
+  LDS_AS uint8_t* const qstage = (LDS_AS uint8_t*)&g_p[0][0];
+  static_assert(sizeof(g_p) >= kMaxRB * 8 * 1024, "Q staging fits in the P buffers");
+  // PV waves: windows 0 and 1, then tiles 0..kStages-1.
+  auto start_stream = [&]() {
     if (nu > 0) load_window(0);
     if (nu > 64) load_window(1);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  }
-  __syncthreads();   // every score wave's Q fragments and page windows have landed
-  if (scorer) {
     pg = g_pages[0][wave][lane];
 #pragma unroll
-    for (int u = 0; u < kStages - 1; ++u) issue_tile(u, pg);
-    const LDS_AS uint8_t* qs = stage_of(kStages - 1) + lane * 16;
+    for (int u = 0; u < kStages; ++u) issue_tile(u, pg);
+  };
+  if (!scorer) {
+    start_stream();
+    wait_dma(pending_after(0, kStages - 1));   // tile 0 (the score waves read it after the barrier)
+  } else {
+    const _Float16* qb = q + (size_t)b * ROWS * kHeadDim;
+    for (int f = wave; f < RB * 8; f += kWaves) {
+      const int row = min(16 * (f >> 3) + n, ROWS - 1);
+      lds_dma16(qb, (unsigned)(row * kHeadDim * 2 + 128 * g + 16 * (f & 7)), qstage + f * 1024);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  __syncthreads();   // Q staged; tile 0 landed
+  if (scorer) {
+    const LDS_AS uint8_t* qs = qstage + lane * 16;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -483,25 +503,16 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
                           fmaxf(g_meta[0][2][row], g_meta[0][3][row]));
       }
       publish_p(0, s);
-      __syncthreads();   // P(0) published
+      __syncthreads();   // P(0) published; tile 1 landed
     }
     for (;;) {
       for (int u = 0; u < nu; ++u) {
-        // Every wave is past tile u's barrier: the stage of tile u-1 is free.
-        const int tn = u + kStages - 1;
-        if (tn < nu) {
-          if ((tn & 63) == 0) {
-            pg = g_pages[(tn >> 6) & 1][wave][lane];
-            if (tn + 64 < nu) load_window((tn >> 6) + 1);
-          }
-          issue_tile(tn, pg);
-        }
         if (u + 1 < nu) {
           float s[RB][4];
           front(u + 1, s);
           publish_p(u + 1, s);
         }
-        __syncthreads();   // P(u+1) published; PV(u) done, so tile u's stage may be refilled
+        __syncthreads();   // P(u+1) published; PV(u) done; tile u+2 landed
       }
       // End of pass: true row max and sum over the four pages (in wave order),
       // the reference, and whether a row outgrew it.
@@ -523,23 +534,17 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
       // Some row max outgrew its reference (P beyond FP16 range somewhere):
       // take the chunk's true row max as the reference and redo the chunk.
       // The reference now bounds every score, so this happens at most once.
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         m_ref[rb] = M[rb];
         l_sum[rb] = 0.f;
         l_cmp[rb] = 0.f;
       }
-      load_window(0);   // this wave's own window buffers: no other wave reads them
-      if (nu > 64) load_window(1);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      pg = g_pages[0][wave][lane];
-#pragma unroll
-      for (int v = 0; v < kStages - 1; ++v) issue_tile(v, pg);
+      __syncthreads();   // restart: tile 0 landed; every read of g_meta / g_flag above is done
       float s[RB][4];
       front(0, s);
       publish_p(0, s);
-      __syncthreads();   // P(0) published; every read of g_meta / g_flag above is done
+      __syncthreads();   // P(0) published; tile 1 landed
     }
     if (wave == 0 && g == 0) {
 #pragma unroll
@@ -548,42 +553,67 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
         if (row < ROWS) {
           const float e = (mref_all[rb] == kNegInf) ? 0.f : fast_exp2((mref_all[rb] - M[rb]) * c2);
           const size_t idx = ((row0 + row) * NS + jsp) * C + chunk;
-          a.st_max[idx] = (M[rb] == kNegInf) ? kNegInf : M[rb] * c;
-          a.st_sum[idx] = lsum[rb] * e * (1.0f / kPScale);
+          __builtin_nontemporal_store((M[rb] == kNegInf) ? kNegInf : M[rb] * c, a.st_max + idx);
+          __builtin_nontemporal_store(lsum[rb] * e * (1.0f / kPScale), a.st_sum + idx);
         }
       }
     }
   } else {
     if (nu > 0) {
       __syncthreads();   // first-tile max exchange
-      __syncthreads();   // P(0) published
+      wait_dma(pending_after(1, kStages - 2));
+      __syncthreads();   // P(0) published; tile 1 landed
     }
     for (;;) {
       for (int u = 0; u < nu; ++u) {
+        // Every wave is past the barrier that ended tile u-1: its stage is free
+        // (tiles 0..kStages-1 went out before the loop).
+        const int tn = u + kStages - 1;
+        if (u > 0 && tn < nu) {
+          if ((tn & 63) == 0) {
+            pg = g_pages[(tn >> 6) & 1][wave][lane];
+            if (tn + 64 < nu) load_window((tn >> 6) + 1);
+          }
+          issue_tile(tn, pg);
+        }
         pv(u);
-        __syncthreads();   // P(u+1) published; PV(u) done
+        wait_dma(pending_after(u + 2, 1));   // tile u+2, which the score waves read next
+        __syncthreads();   // P(u+1) published; PV(u) done; tile u+2 landed
       }
       __syncthreads();   // end-of-pass meta written
       if (!read_meta()) break;
+      // Restart (see the score waves): refill the ring from the first tile.
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) o[mb][rb] = float4v{0.f, 0.f, 0.f, 0.f};
-      __syncthreads();   // restart: P(0) published
+      start_stream();
+      wait_dma(pending_after(0, kStages - 1));
+      __syncthreads();   // restart: tile 0 landed
+      wait_dma(pending_after(1, kStages - 2));
+      __syncthreads();   // P(0) published; tile 1 landed
     }
-    // Renormalise to the true row max and store this wave's dimensions.
+    // Renormalise to the true row max; this wave's dimensions of every row go
+    // to LDS (the ring is idle: every tile has been consumed).
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const int row = 16 * rb + n;
-      if (row < ROWS) {
-        const float e = (mref_all[rb] == kNegInf) ? 0.f : fast_exp2((mref_all[rb] - M[rb]) * c2);
-        const size_t idx = ((row0 + row) * NS + jsp) * C + chunk;
-        const float of = e * ofac;
+      const float e = (mref_all[rb] == kNegInf) ? 0.f : fast_exp2((mref_all[rb] - M[rb]) * c2);
+      const float of = e * ofac;
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-          *(float4v*)(a.st_num + idx * kHeadDim + 16 * (4 * wave + mb) + 4 * g) = o[mb][rb] * of;
-      }
+      for (int mb = 0; mb < 4; ++mb)
+        *(LDS_AS float4v*)(g_ring + row * kORowBytes + 4 * (16 * (4 * wave + mb) + 4 * g)) = o[mb][rb] * of;
     }
+  }
+  // Numerator rows leave as whole 1 KB rows, one row per wave instruction.
+  // The stores are non-temporal: nothing in this launch reads them back, and
+  // streamed out they no longer pile up as dirty cache lines that the end of
+  // the launch would have to write back all at once.
+  __syncthreads();
+  for (int row = wid; row < ROWS; row += 2 * kWaves) {
+    const size_t idx = ((row0 + row) * NS + jsp) * C + chunk;
+    __builtin_nontemporal_store(*(const LDS_AS float4v*)(g_ring + row * kORowBytes + 16 * lane),
+                                (float4v*)(a.st_num + idx * kHeadDim + 4 * lane));
   }
 }
 
