@@ -109,6 +109,14 @@ __device__ __forceinline__ float sum_x32(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// max(a, b, c) in one instruction.  Scores are finite or -inf, never NaN, so the
+// NaN-quieting copies that fmaxf would add are not needed.
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 // Neumaier compensated add of x into (sum, comp).
 __device__ __forceinline__ void comp_add(float& sum, float& comp, float x) {
   const float t = sum + x;
@@ -290,31 +298,36 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
   };
 
   half8 qf[RB][8];       // Q in MFMA B-operand order (score waves; AGPRs)
-  float m_ref[RB], m_lane[RB], l_sum[RB], l_cmp[RB];
+  // m_ref: the row's reference max (-inf until known, and for a row that sees no
+  // key of the chunk); mr: m_ref, or 0 for such a row; m_lane: this lane's
+  // largest s - mr.
+  float m_ref[RB], mr[RB], m_lane[RB], l_sum[RB], l_cmp[RB];
   int pg = 0;
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     m_ref[rb] = kNegInf;
+    mr[rb] = 0.f;
     m_lane[rb] = kNegInf;
     l_sum[rb] = 0.f;
     l_cmp[rb] = 0.f;
   }
   const unsigned kswz = 16u * (unsigned)n;   // K row n, chunk (4g+i)^n, as n*256 + 16*((4g+i)^n)
 
-  // S^T = K_w * Q^T for this wave's page of tile t; lane holds keys
-  // key_lo + 64t + 16w + 4g + r of row 16rb + n.  Masked keys get -inf.
+  // S^T - mr = K_w * Q^T - mr for this wave's page of tile t (the products
+  // accumulate onto -mr); lane holds keys key_lo + 64t + 16w + 4g + r of row
+  // 16rb + n.  Masked keys get -inf.
   auto qk = [&](int t, float (&s)[RB][4]) {
     float4v sacc[RB];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) sacc[rb] = float4v{0.f, 0.f, 0.f, 0.f};
+    for (int rb = 0; rb < RB; ++rb) sacc[rb] = float4v{-mr[rb], -mr[rb], -mr[rb], -mr[rb]};
     const LDS_AS uint8_t* krow = stage_of(t) + wave * kPageBytes + n * 256;
-    uint4v kr = *(const LDS_AS uint4v*)(krow + ((16u * (4 * g)) ^ kswz));
+    uint4v kr[4];   // all four reads in flight at once: one LDS latency per tile
+#pragma unroll
+    for (int i = 0; i < 4; ++i) kr[i] = *(const LDS_AS uint4v*)(krow + ((16u * (4 * g + i)) ^ kswz));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint4v cur = kr;
-      if (i < 3) kr = *(const LDS_AS uint4v*)(krow + ((16u * (4 * g + i + 1)) ^ kswz));
-      const half8 k0 = decode8(cur[0], cur[1]);
-      const half8 k1 = decode8(cur[2], cur[3]);
+      const half8 k0 = decode8(kr[i][0], kr[i][1]);
+      const half8 k1 = decode8(kr[i][2], kr[i][3]);
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
         sacc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, qf[rb][2 * i], sacc[rb], 0, 0, 0);
@@ -335,25 +348,23 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
           if (kb + r > limit[rb]) s[rb][r] = kNegInf;
     }
   };
-  // Running max of this lane's keys (cross-lane reduction only at the chunk end).
+  // Running max of this lane's s - mr (cross-lane reduction only at the chunk end).
   auto lane_max = [&](const float (&s)[RB][4]) {
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-      m_lane[rb] = fmaxf(fmaxf(m_lane[rb], fmaxf(s[rb][0], s[rb][1])), fmaxf(s[rb][2], s[rb][3]));
+    for (int rb = 0; rb < RB; ++rb) m_lane[rb] = max3(max3(m_lane[rb], s[rb][0], s[rb][1]), s[rb][2], s[rb][3]);
   };
-  // P * 2^3 = exp2((s - m_ref) * c2 + 3) as FP16 hi (truncated) + FP16 lo (the
-  // exact remainder, rounded); compensated row sums.  (s - m_ref) first: exact
-  // for keys near the max, so P keeps full relative precision even when
-  // |m_ref * c2| is large.  Published for every PV wave: operand (ks, rb,
-  // hi|lo), lane (n, g), halves 4(w%2)..+3, ks = w/2.
+  // P * 2^3 = exp2((s - mr) * c2 + 3) as FP16 hi (truncated) + FP16 lo (the
+  // exact remainder, rounded); compensated row sums.  s - mr comes straight
+  // from the accumulation, so keys near the max keep full relative precision
+  // even when |m_ref * c2| is large.  Published for every PV wave: operand
+  // (ks, rb, hi|lo), lane (n, g), halves 4(w%2)..+3, ks = w/2.
   auto publish_p = [&](int t, const float (&s)[RB][4]) {
     LDS_AS uint8_t* pw = (LDS_AS uint8_t*)g_p[t & 1] + lane * 16 + 8 * (wave & 1);
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      const float mr = (m_ref[rb] == kNegInf) ? 0.f : m_ref[rb];   // a row without keys has s = -inf
       float p8[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) p8[r] = fast_exp2(__builtin_fmaf(s[rb][r] - mr, c2, kPScaleLog2));
+      for (int r = 0; r < 4; ++r) p8[r] = fast_exp2(__builtin_fmaf(s[rb][r], c2, kPScaleLog2));
       const half2v h01 = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(p8[0], p8[1]));
       const half2v h23 = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(p8[2], p8[3]));
       const half4 hi = half4{h01[0], h01[1], h23[0], h23[1]};
@@ -366,12 +377,11 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
       *(LDS_AS half4*)(pw + (slot + 1) * kPSlot) = lo;
     }
   };
-  // Scores of tile t up to (not including) publishing: tail, QK, maxima.  The
-  // PV waves have waited for the tile's DMAs before the barrier that precedes.
+  // Scores of tile t up to (not including) publishing: tail, QK.  The PV waves
+  // have waited for the tile's DMAs before the barrier that precedes.
   auto front = [&](int t, float (&s)[RB][4]) {
     if (key_lo + kTileKeys * (t + 1) > key_end) clear_tail(t);
     qk(t, s);
-    lane_max(s);
   };
 
   // ------------------------------------------------------------------ PV waves
@@ -396,9 +406,18 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
   // PV of tile t: 64 keys as two 32-key MFMA steps (pages 2ks, 2ks+1), for
   // this wave's four 16-dimension blocks; hi products of every row block first,
   // then lo, so dependent MFMAs on one accumulator are RB instructions apart.
-  auto pv = [&](int t) {
+  //
+  // When tn >= 0 the eight 1 KB loads of this wave's page of tile tn (K, then
+  // V) are issued one per 16-dimension block, between the products: issued
+  // back to back they would wait for the CU's address unit (about one 1 KB
+  // instruction per 16 cycles, shared by the four PV waves) and stall the wave.
+  auto pv = [&](int t, int tn) {
     const unsigned sbase = (unsigned)(uintptr_t)stage_of(t);
     const LDS_AS uint8_t* pr = (const LDS_AS uint8_t*)g_p[t & 1] + lane * 16;
+    const bool dma = tn >= 0 && tile_valid(tn);
+    const int page = dma ? __builtin_amdgcn_readlane(pg, tn & 63) : 0;
+    const uint8_t* kvp[2] = {k_cache + (size_t)page * kPageBytes, v_cache + (size_t)page * kPageBytes};
+    LDS_AS uint8_t* dst = stage_of(dma ? tn : 0) + wave * kPageBytes;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       half8 phi[RB], plo[RB];
@@ -407,11 +426,15 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
         phi[rb] = *(const LDS_AS half8*)(pr + ((ks * RB + rb) * 2) * kPSlot);
         plo[rb] = *(const LDS_AS half8*)(pr + ((ks * RB + rb) * 2 + 1) * kPSlot);
       }
+      int2v vr[4];
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+        vr[mb] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (LDS_AS int2v*)(uintptr_t)(sbase + ks * 2 * kPageBytes + voff[mb]));
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
-        const int2v vr = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-            (LDS_AS int2v*)(uintptr_t)(sbase + ks * 2 * kPageBytes + voff[mb]));
-        const half8 va = decode8((unsigned)vr[0], (unsigned)vr[1]);
+        if (dma) lds_dma16(kvp[ks], lane_off[mb], dst + ks * kVOffset + mb * 1024);
+        const half8 va = decode8((unsigned)vr[mb][0], (unsigned)vr[mb][1]);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
           o[mb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, phi[rb], o[mb][rb], 0, 0, 0);
@@ -488,10 +511,10 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
     // (every row that sees any key of the chunk sees its first key).
     if (nu > 0) {
       float s[RB][4];
-      front(0, s);
+      front(0, s);   // mr = 0 still: plain scores
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        const float t = fmaxf(fmaxf(s[rb][0], s[rb][1]), fmaxf(s[rb][2], s[rb][3]));
+        const float t = max3(max3(kNegInf, s[rb][0], s[rb][1]), s[rb][2], s[rb][3]);
         const float tm = max_x32(max_x16(t));
         if (g == 0) g_meta[0][wave][16 * rb + n] = tm;
       }
@@ -501,7 +524,11 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
         const int row = 16 * rb + n;
         m_ref[rb] = fmaxf(fmaxf(g_meta[0][0][row], g_meta[0][1][row]),
                           fmaxf(g_meta[0][2][row], g_meta[0][3][row]));
+        mr[rb] = (m_ref[rb] == kNegInf) ? 0.f : m_ref[rb];   // a row without keys has s = -inf
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s[rb][r] -= mr[rb];
       }
+      lane_max(s);
       publish_p(0, s);
       __syncthreads();   // P(0) published; tile 1 landed
     }
@@ -510,6 +537,7 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
         if (u + 1 < nu) {
           float s[RB][4];
           front(u + 1, s);
+          lane_max(s);
           publish_p(u + 1, s);
         }
         __syncthreads();   // P(u+1) published; PV(u) done; tile u+2 landed
@@ -519,8 +547,8 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
       bool ovf = false;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        ovf |= (m_lane[rb] - m_ref[rb]) * c2 > kRestartLog2;   // false while -inf
-        const float mx = max_x32(max_x16(m_lane[rb]));
+        ovf |= m_lane[rb] * c2 > kRestartLog2;   // false while -inf
+        const float mx = mr[rb] + max_x32(max_x16(m_lane[rb]));   // -inf stays -inf
         const float l = sum_x32(sum_x16(l_sum[rb])) + sum_x32(sum_x16(l_cmp[rb]));
         if (g == 0) {
           g_meta[0][wave][16 * rb + n] = mx;
@@ -537,12 +565,15 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         m_ref[rb] = M[rb];
+        mr[rb] = (M[rb] == kNegInf) ? 0.f : M[rb];
+        m_lane[rb] = kNegInf;
         l_sum[rb] = 0.f;
         l_cmp[rb] = 0.f;
       }
       __syncthreads();   // restart: tile 0 landed; every read of g_meta / g_flag above is done
       float s[RB][4];
       front(0, s);
+      lane_max(s);
       publish_p(0, s);
       __syncthreads();   // P(0) published; tile 1 landed
     }
@@ -569,14 +600,15 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
         // Every wave is past the barrier that ended tile u-1: its stage is free
         // (tiles 0..kStages-1 went out before the loop).
         const int tn = u + kStages - 1;
+        int tdma = -1;
         if (u > 0 && tn < nu) {
           if ((tn & 63) == 0) {
             pg = g_pages[(tn >> 6) & 1][wave][lane];
             if (tn + 64 < nu) load_window((tn >> 6) + 1);
           }
-          issue_tile(tn, pg);
+          tdma = tn;
         }
-        pv(u);
+        pv(u, tdma);
         wait_dma(pending_after(u + 2, 1));   // tile u+2, which the score waves read next
         __syncthreads();   // P(u+1) published; PV(u) done; tile u+2 landed
       }
