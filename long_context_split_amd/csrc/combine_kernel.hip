@@ -29,6 +29,9 @@ namespace {
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr int kCombineWaves = 8;
+constexpr int kGroupsPerBatch = 3;   // 4-split groups per wave per load batch
+
+typedef float float4v __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
@@ -38,59 +41,68 @@ __device__ __forceinline__ float wave_max(float x) {
 
 // C = chunks per split in the source (1: the source is the workspace itself).
 // OUT = form the FP16 output (else only merge chunk states into the workspace).
+// Lane (k, d) = (lane / 16, lane % 16) covers split 4*gi + k of each of its
+// wave's split groups gi and dimensions 64*quarter + 4d .. +3.
 template <int C, bool OUT>
 __global__ __launch_bounds__(kCombineWaves * 64) void combine_kernel(CombineArgs a) {
-  constexpr int kBatch = C == 1 ? 16 : (C == 2 ? 12 : 10);   // splits per wave per load batch
-  __shared__ float s_num[kCombineWaves][64];
+  __shared__ float4v s_num[kCombineWaves][16];
   __shared__ float s_den[kCombineWaves];
   const int row = blockIdx.x >> 2;
   const int quarter = blockIdx.x & 3;
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
+  const int k = lane >> 4;
+  const int d = lane & 15;
   const int NS = a.num_splits;
+  const int NG = (NS + 3) >> 2;
   const float* mrow = a.src_max + (size_t)row * NS * C;
   const float* lrow = a.src_sum + (size_t)row * NS * C;
-  const float* orow = a.src_num + (size_t)row * NS * C * kHeadDim + 64 * quarter + lane;
+  const float* orow = a.src_num + (size_t)row * NS * C * kHeadDim + 64 * quarter + 4 * d;
 
   float M = kNegInf;
-  float num = 0.f, den = 0.f;
-  for (int j0 = wave; j0 < NS; j0 += kCombineWaves * kBatch) {
-    float mv[kBatch][C], lv[kBatch][C], ov[kBatch][C];
+  float4v num = float4v{0.f, 0.f, 0.f, 0.f};
+  float den = 0.f;
+  for (int g0 = wave; g0 < NG; g0 += kCombineWaves * kGroupsPerBatch) {
+    float4v ov[kGroupsPerBatch][C];
+    float mv[kGroupsPerBatch][C], lv[kGroupsPerBatch][C];
 #pragma unroll
-    for (int k = 0; k < kBatch; ++k) {
-      const int j = j0 + kCombineWaves * k;
+    for (int b = 0; b < kGroupsPerBatch; ++b) {
+      const int j = 4 * (g0 + kCombineWaves * b) + k;
+      const bool in = j < NS;
+      const size_t s0 = (size_t)(in ? j : 0) * C;
 #pragma unroll
       for (int c = 0; c < C; ++c) {
-        const bool in = j < NS;
-        const size_t s = (size_t)(in ? j : 0) * C + c;
-        ov[k][c] = orow[s * kHeadDim];
-        mv[k][c] = in ? mrow[s] : kNegInf;
-        lv[k][c] = lrow[s];
+        ov[b][c] = *(const float4v*)(orow + (s0 + c) * kHeadDim);
+        mv[b][c] = mrow[s0 + c];
+        lv[b][c] = lrow[s0 + c];
+        if (!in) mv[b][c] = kNegInf;
       }
     }
-    if (OUT && j0 == wave) {   // row max over every state, while the batch is in flight
-      for (int j = lane; j < NS * C; j += 64) M = fmaxf(M, mrow[j]);
+    if (OUT && g0 == wave) {   // row max over every state, while the batch is in flight
+      for (int s = lane; s < NS * C; s += 64) M = fmaxf(M, mrow[s]);
       M = wave_max(M);
     }
 #pragma unroll
-    for (int k = 0; k < kBatch; ++k) {
-      const int j = j0 + kCombineWaves * k;
-      float mj = mv[k][0], lj = lv[k][0], oj = ov[k][0];
+    for (int b = 0; b < kGroupsPerBatch; ++b) {
+      const int j = 4 * (g0 + kCombineWaves * b) + k;
+      float mj = mv[b][0], lj = lv[b][0];
+      float4v oj = ov[b][0];
       if (C > 1) {
 #pragma unroll
-        for (int c = 1; c < C; ++c) mj = fmaxf(mj, mv[k][c]);
+        for (int c = 1; c < C; ++c) mj = fmaxf(mj, mv[b][c]);
         lj = 0.f;
-        oj = 0.f;
+        oj = float4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < C; ++c) {
-          const float e = (mv[k][c] == kNegInf) ? 0.f : __expf(mv[k][c] - mj);
-          lj = __builtin_fmaf(lv[k][c], e, lj);
-          oj = __builtin_fmaf(ov[k][c], e, oj);
+          const float e = (mv[b][c] == kNegInf) ? 0.f : __expf(mv[b][c] - mj);
+          lj = __builtin_fmaf(lv[b][c], e, lj);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) oj[i] = __builtin_fmaf(ov[b][c][i], e, oj[i]);
         }
         if (j < NS) {
           const size_t w = (size_t)row * NS + j;
-          __builtin_nontemporal_store(oj, a.ws_num + w * kHeadDim + 64 * quarter + lane);
-          if (quarter == 0 && lane == 0) {
+          __builtin_nontemporal_store(oj, (float4v*)(a.ws_num + w * kHeadDim + 64 * quarter + 4 * d));
+          if (quarter == 0 && d == 0) {
             __builtin_nontemporal_store(mj, a.ws_max + w);
             __builtin_nontemporal_store(lj, a.ws_sum + w);
           }
@@ -98,23 +110,34 @@ __global__ __launch_bounds__(kCombineWaves * 64) void combine_kernel(CombineArgs
       }
       if (OUT) {
         const float e = (mj == kNegInf) ? 0.f : __expf(mj - M);
-        num = __builtin_fmaf(oj, e, num);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) num[i] = __builtin_fmaf(oj[i], e, num[i]);
         den = __builtin_fmaf(lj, e, den);
       }
     }
   }
   if (!OUT) return;
-  s_num[wave][lane] = num;
+  // Splits 4g + k, then the four k (pairwise), then the waves, all in fixed order.
+#pragma unroll
+  for (int off = 16; off <= 32; off <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) num[i] += __shfl_xor(num[i], off, 64);
+    den += __shfl_xor(den, off, 64);
+  }
+  if (lane < 16) s_num[wave][lane] = num;
   if (lane == 0) s_den[wave] = den;
   __syncthreads();
-  if (wave == 0) {
-    float n = 0.f, d = 0.f;
+  if (wave == 0 && lane < 16) {
+    float4v n = float4v{0.f, 0.f, 0.f, 0.f};
+    float dd = 0.f;
 #pragma unroll
     for (int v = 0; v < kCombineWaves; ++v) {
       n += s_num[v][lane];
-      d += s_den[v];
+      dd += s_den[v];
     }
-    a.out[(size_t)row * kHeadDim + 64 * quarter + lane] = (_Float16)(n / d);
+    _Float16* o = a.out + (size_t)row * kHeadDim + 64 * quarter + 4 * lane;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = (_Float16)(n[i] / dd);
   }
 }
 

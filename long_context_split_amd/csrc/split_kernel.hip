@@ -23,8 +23,8 @@
 //     (global_load_lds_dwordx4); the first four tiles go out as soon as the
 //     block table has arrived, and afterwards two tiles are in flight while
 //     one is scored and one is multiplied into V.  Inside a 256-byte token row
-//     the 16-byte chunks are XOR-swizzled by the row's page slot so operand
-//     reads are conflict free.
+//     the 16-byte chunks are XOR-swizzled by the row's slot and the page's
+//     parity so operand reads are conflict free.
 //   * Eight waves, two per SIMD, split each tile by role.  For QK^T score wave
 //     w takes page w: S^T = K_w * Q^T on v_mfma_f32_16x16x32_f16 for all 6q rows
 //     (up to three 16-row blocks, Q held in registers), so every K byte is
@@ -233,12 +233,15 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
 
   // ------------------------------------------------------------------ score waves
   // DMA lane offsets: load qq of a page fills LDS row r = 4qq + lane/16, chunk
-  // position lane%16, with global chunk (lane%16) ^ r of that row.
+  // position lane%16, with global chunk (lane%16) ^ r ^ x of that row, where
+  // x = 4 * (page slot & 1): the two pages that one 32-key PV step reads
+  // together then use different banks for the same row.
+  const unsigned xpage = 4u * (unsigned)(wave & 1);
   unsigned lane_off[4];
 #pragma unroll
   for (int qq = 0; qq < 4; ++qq) {
     const unsigned r = 4 * qq + (lane >> 4);
-    lane_off[qq] = r * 256u + 16u * ((unsigned)(lane & 15) ^ r);
+    lane_off[qq] = r * 256u + 16u * ((unsigned)(lane & 15) ^ r ^ xpage);
   }
   // Wave w's page of tile u is page_lo + 4u + w; pages past the chunk are skipped.
   auto tile_valid = [&](int u) { return u < nu && page_lo + 4 * u + wave < page_end; };
@@ -311,7 +314,7 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
     l_sum[rb] = 0.f;
     l_cmp[rb] = 0.f;
   }
-  const unsigned kswz = 16u * (unsigned)n;   // K row n, chunk (4g+i)^n, as n*256 + 16*((4g+i)^n)
+  const unsigned kswz = 16u * ((unsigned)n ^ xpage);   // K row n, chunk c at n*256 + 16*(c ^ n ^ x)
 
   // S^T - mr = K_w * Q^T - mr for this wave's page of tile t (the products
   // accumulate onto -mr); lane holds keys key_lo + 64t + 16w + 4g + r of row
@@ -398,10 +401,11 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
   {
     const int vj = n >> 1;
     const int vslot = 4 * g + (vj & 3);
+    const unsigned vx = 4u * (unsigned)(vj >> 2);   // x of page 2ks + j/4
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
       voff[mb] = kVOffset + (vj >> 2) * kPageBytes + vslot * 256 + 8 * (n & 1) +
-                 ((16u * (4 * wave + mb)) ^ (16u * vslot));
+                 ((16u * (4 * wave + mb)) ^ (16u * ((unsigned)vslot ^ vx)));
   }
   // PV of tile t: 64 keys as two 32-key MFMA steps (pages 2ks, 2ks+1), for
   // this wave's four 16-dimension blocks; hi products of every row block first,
