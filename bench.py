@@ -125,10 +125,6 @@ def main():
             dfv.attn_split_chunks(desc, inp.q, inp.k_cache, inp.v_cache, inp.block_table,
                                   inp.context_lens, inp.k_scale, inp.v_scale, *cb, stream)
 
-    def combine_only():
-        for ws in wss:
-            dfv.attn_combine(desc, ws.ws_max, ws.ws_sum, ws.ws_num, ws.out, stream)
-
     def timed(fn, reps):
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
@@ -158,12 +154,11 @@ def main():
     ms_per_step = total_ms / args.steps
 
     # dominant kernel alone (the split kernel writing key-chunk states), then the
-    # split stage (split kernel + chunk merge) and the combine, same stream, same layers
+    # split stage (split kernel + chunk merge), same stream, same layers
     for _ in range(args.warmup):
         split_kernel_only()
     kernel_ms = timed(split_kernel_only, args.steps) / (args.steps * len(layers))
     split_ms = timed(split_only, args.steps) / (args.steps * len(layers))
-    combine_ms = timed(combine_only, args.steps) / (args.steps * len(layers))
 
     kv_bytes_layer = 2 * L * 256          # K + V E4M3 bytes per layer: 512 B per context token
     nrows = nq * 6
@@ -194,7 +189,6 @@ def main():
         "split_kernel_ms_per_launch": round(kernel_ms, 5),
         "split_stage_ms_per_call": round(split_ms, 5),
         "key_chunks_per_split": dfv.chunks(desc),
-        "combine_ms_per_launch": round(combine_ms, 5),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,
