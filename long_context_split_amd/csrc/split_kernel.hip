@@ -78,6 +78,8 @@ constexpr int kVOffset = 4 * kPageBytes;
 constexpr int kPSlot = 64 * 16;              // one (k-step, row block, hi|lo) P operand: 64 lanes x 16 B
 constexpr int kSplitThreads = 2 * kThreads;  // four score waves + four PV waves, two per SIMD
 constexpr int kORowBytes = 4 * kHeadDim + 16;  // numerator row staged in LDS; the pad spreads 16 rows over all banks
+constexpr int kORowsPerStage = kTileBytes / kORowBytes;   // 31 rows of one ring stage
+static_assert(2 * kORowsPerStage >= kMaxRows, "two ring stages hold the staged numerator rows");
 
 // Eight E4M3 codes (two dwords) to eight FP16 values, two codes per instruction.
 __device__ __forceinline__ half8 decode8(unsigned lo, unsigned hi) {
@@ -449,6 +451,21 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
     }
   };
 
+  // The numerator rows of the finished chunk, unscaled, in the two ring stages
+  // that the last tile does not occupy (rows 0..30 in one, 31..47 in the
+  // other); no load targets them any more once the last tile is in flight.
+  auto ostage = [&](int row) {
+    return row < kORowsPerStage ? stage_of(nu) + row * kORowBytes
+                                : stage_of(nu + 1) + (row - kORowsPerStage) * kORowBytes;
+  };
+  auto stage_o = [&]() {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+        *(LDS_AS float4v*)(ostage(16 * rb + n) + 4 * (16 * (4 * wave + mb) + 4 * g)) = o[mb][rb];
+  };
+
   // ------------------------------------------------------------------ prologue
   // The PV waves own the DMA stream: PV wave w fetches the block-table windows
   // of page w (0 and 1) and, as soon as those land, puts page w of the first
@@ -536,18 +553,10 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
       publish_p(0, s);
       __syncthreads();   // P(0) published; tile 1 landed
     }
-    for (;;) {
-      for (int u = 0; u < nu; ++u) {
-        if (u + 1 < nu) {
-          float s[RB][4];
-          front(u + 1, s);
-          lane_max(s);
-          publish_p(u + 1, s);
-        }
-        __syncthreads();   // P(u+1) published; PV(u) done; tile u+2 landed
-      }
-      // End of pass: true row max and sum over the four pages (in wave order),
-      // the reference, and whether a row outgrew it.
+    // End of pass: true row max and sum over the four pages (in wave order),
+    // the reference, and whether a row outgrew it.  Written while the PV
+    // waves work on the last tile, published by the barrier that ends it.
+    auto end_meta = [&]() {
       bool ovf = false;
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
@@ -561,7 +570,23 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
         }
       }
       g_flag[wave] = __builtin_amdgcn_ballot_w64(ovf) != 0;
-      __syncthreads();
+    };
+    for (;;) {
+      for (int u = 0; u < nu; ++u) {
+        if (u + 1 < nu) {
+          float s[RB][4];
+          front(u + 1, s);
+          lane_max(s);
+          publish_p(u + 1, s);
+        } else {
+          end_meta();
+        }
+        __syncthreads();   // P(u+1) published (meta, after the last tile); PV(u) done; tile u+2 landed
+      }
+      if (nu == 0) {
+        end_meta();
+        __syncthreads();
+      }
       if (!read_meta()) break;
       // Some row max outgrew its reference (P beyond FP16 range somewhere):
       // take the chunk's true row max as the reference and redo the chunk.
@@ -613,10 +638,16 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
           tdma = tn;
         }
         pv(u, tdma);
-        wait_dma(pending_after(u + 2, 1));   // tile u+2, which the score waves read next
-        __syncthreads();   // P(u+1) published; PV(u) done; tile u+2 landed
+        if (u + 1 < nu)
+          wait_dma(pending_after(u + 2, 1));   // tile u+2, which the score waves read next
+        else
+          stage_o();
+        __syncthreads();   // P(u+1) published (meta, after the last tile); PV(u) done; tile u+2 landed
       }
-      __syncthreads();   // end-of-pass meta written
+      if (nu == 0) {
+        stage_o();
+        __syncthreads();
+      }
       if (!read_meta()) break;
       // Restart (see the score waves): refill the ring from the first tile.
 #pragma unroll
@@ -629,26 +660,18 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
       wait_dma(pending_after(1, kStages - 2));
       __syncthreads();   // P(0) published; tile 1 landed
     }
-    // Renormalise to the true row max; this wave's dimensions of every row go
-    // to LDS (the ring is idle: every tile has been consumed).
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const int row = 16 * rb + n;
-      const float e = (mref_all[rb] == kNegInf) ? 0.f : fast_exp2((mref_all[rb] - M[rb]) * c2);
-      const float of = e * ofac;
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-        *(LDS_AS float4v*)(g_ring + row * kORowBytes + 4 * (16 * (4 * wave + mb) + 4 * g)) = o[mb][rb] * of;
-    }
   }
-  // Numerator rows leave as whole 1 KB rows, one row per wave instruction.
-  // The stores are non-temporal: nothing in this launch reads them back, and
-  // streamed out they no longer pile up as dirty cache lines that the end of
-  // the launch would have to write back all at once.
-  __syncthreads();
+  // Numerator rows leave as whole 1 KB rows, one row per wave instruction,
+  // renormalised to the true row max on the way.  The stores are
+  // non-temporal: nothing in this launch reads them back, and streamed out
+  // they no longer pile up as dirty cache lines that the end of the launch
+  // would have to write back all at once.
   for (int row = wid; row < ROWS; row += 2 * kWaves) {
+    const float mx = fmaxf(fmaxf(g_meta[0][0][row], g_meta[0][1][row]), fmaxf(g_meta[0][2][row], g_meta[0][3][row]));
+    const float rf = g_meta[2][0][row];
+    const float of = (rf == kNegInf) ? 0.f : fast_exp2((rf - mx) * c2) * ofac;
     const size_t idx = ((row0 + row) * NS + jsp) * C + chunk;
-    __builtin_nontemporal_store(*(const LDS_AS float4v*)(g_ring + row * kORowBytes + 16 * lane),
+    __builtin_nontemporal_store(*(const LDS_AS float4v*)(ostage(row) + 16 * lane) * of,
                                 (float4v*)(a.st_num + idx * kHeadDim + 4 * lane));
   }
 }
