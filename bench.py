@@ -5,10 +5,14 @@ One step is the whole hot path over one batch of synthetic input: for each of
 kernel (80 logical splits, FP32 workspace) and the combine kernel, launched
 back to back on one stream.  Inputs are resident in HBM before timing starts.
 
-Printed: one JSON line with the headline metric (ms per 16-layer attention),
-the roofline of the dominant kernel (split kernel: algorithmic KV bytes per
-launch / its average launch time, measured with HIP events on the launch
-stream), and the CPU oracle's time on a bounded sample (rank 0, N=1 only).
+Printed: one JSON line with the headline metric (ms per 16-layer attention;
+also its per-step median/p10/p90 and the same step replayed as a captured HIP
+graph), the roofline of the dominant kernel (split kernel: algorithmic KV
+bytes per launch / its average launch time, measured with HIP events on the
+launch stream), the split stage and the combine alone, the small-q sweep
+(q = 1..7 over the same KV), the box's page-read ceiling (a probe that streams
+exactly the layer's K and V pages in block-table order and computes nothing),
+and the CPU oracle's time on a bounded sample (rank 0, N=1 only).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--no-cpu-baseline] [--graph]
@@ -16,6 +20,8 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 from __future__ import annotations
 
 import argparse
+import ctypes
+import dataclasses
 import hashlib
 import json
 import os
@@ -29,8 +35,7 @@ HBM_PEAK_GBPS = 8000.0          # MI355X published HBM3E bandwidth
 V100_16LAYER_MS = 12.983        # the pages' 16-layer q8 attention on V100 (context only)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "split_kernel_traffic.json")
 SPLIT_SRCS = [os.path.join(ROOT, "long_context_split_amd", "csrc", "split_kernel.hip"),
-              os.path.join(ROOT, "long_context_split_amd", "csrc", "dfv_common.h"),
-              os.path.join(ROOT, "long_context_split_amd", "build.py")]
+              os.path.join(ROOT, "long_context_split_amd", "csrc", "dfv_common.h")]
 
 
 def parse():
@@ -41,7 +46,10 @@ def parse():
     p.add_argument("--workload", default="ctx261888_16layer")
     p.add_argument("--num-q", type=int, default=None)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--graph", action="store_true", help="time a captured HIP graph of the step")
+    p.add_argument("--graph", action="store_true", help="report the captured-graph step time as the value")
+    p.add_argument("--no-sweep", action="store_true", help="skip the small-q sweep")
+    p.add_argument("--no-extras", action="store_true",
+                   help="time the step and the split kernel only (no graphs, sweep or probe; for counter runs)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="after timing, run a plain 512 MiB device-to-device copy (reference for HBM counters)")
     return p.parse_args()
@@ -49,10 +57,12 @@ def parse():
 
 def src_hash() -> str:
     """Hash of everything that shapes the split kernel's binary (source, shared header, flags)."""
+    from long_context_split_amd import build as B
     h = hashlib.sha256()
     for p in SPLIT_SRCS:
         with open(p, "rb") as f:
             h.update(f.read())
+    h.update(" ".join(B.HIPCC_FLAGS).encode())
     return h.hexdigest()[:16]
 
 
@@ -95,6 +105,7 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library has no "
               "multi-GPU path.", file=sys.stderr)
         sys.exit(2)
+    import numpy as np
     import torch
     from long_context_split_amd import dfv, synth
 
@@ -111,60 +122,115 @@ def main():
     cbufs = [dfv.chunk_buffers(desc) for _ in layers]
     stream = torch.cuda.current_stream()
 
+    # Every call takes the current stream at call time, so the same functions
+    # run eagerly and under graph capture.
     def step():
         for inp, ws in zip(layers, wss):
-            dfv.run_layer(inp, ws, desc, stream)
+            dfv.run_layer(inp, ws, desc)
 
     def split_only():
         for inp, ws in zip(layers, wss):
             dfv.attn_split(desc, inp.q, inp.k_cache, inp.v_cache, inp.block_table, inp.context_lens,
-                           inp.k_scale, inp.v_scale, ws.ws_max, ws.ws_sum, ws.ws_num, ws.scratch, stream)
+                           inp.k_scale, inp.v_scale, ws.ws_max, ws.ws_sum, ws.ws_num, ws.scratch)
+
+    def combine_only():
+        for ws in wss:
+            dfv.attn_combine(desc, ws.ws_max, ws.ws_sum, ws.ws_num, ws.out)
 
     def split_kernel_only():
         for inp, cb in zip(layers, cbufs):
             dfv.attn_split_chunks(desc, inp.q, inp.k_cache, inp.v_cache, inp.block_table,
-                                  inp.context_lens, inp.k_scale, inp.v_scale, *cb, stream)
+                                  inp.context_lens, inp.k_scale, inp.v_scale, *cb)
 
     def timed(fn, reps):
+        """Total ms of `reps` calls, and the ms of each, from HIP events on the stream."""
+        cur = torch.cuda.current_stream()
         torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(reps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record(cur)
+        for r in range(reps):
             fn()
-        e1.record(stream)
+            ev[r + 1].record(cur)
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1)
+        return ev[0].elapsed_time(ev[-1]), [ev[r].elapsed_time(ev[r + 1]) for r in range(reps)]
+
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        torch.cuda.synchronize()
+        for _ in range(max(1, args.warmup)):
+            g.replay()
+        torch.cuda.synchronize()
+        return g
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    graph = None
-    if args.graph:
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            step()
-        for _ in range(args.warmup):
-            graph.replay()
-        torch.cuda.synchronize()
-        run = graph.replay
-    else:
-        run = step
-    total_ms = timed(run, args.steps)
+    stream_total, stream_steps = timed(step, args.steps)
+    graph_total, graph_steps = (None, None)
+    if not args.no_extras or args.graph:
+        graph_total, graph_steps = timed(capture(step).replay, args.steps)
+    total_ms, per_step = (graph_total, graph_steps) if args.graph else (stream_total, stream_steps)
     ms_per_step = total_ms / args.steps
+    q10, q50, q90 = (float(x) for x in np.percentile(np.asarray(per_step), [10, 50, 90]))
 
-    # dominant kernel alone (the split kernel writing key-chunk states), then the
-    # split stage (split kernel + chunk merge), same stream, same layers
+    # dominant kernel alone (the split kernel writing key-chunk states), launched
+    # on the stream; then the split stage and the combine alone as graph replays
     for _ in range(args.warmup):
         split_kernel_only()
-    kernel_ms = timed(split_kernel_only, args.steps) / (args.steps * len(layers))
-    split_ms = timed(split_only, args.steps) / (args.steps * len(layers))
+    kernel_ms = timed(split_kernel_only, args.steps)[0] / (args.steps * len(layers))
+    split_ms = combine_ms = None
+    if not args.no_extras:
+        split_ms = timed(capture(split_only).replay, args.steps)[0] / (args.steps * len(layers))
+        combine_ms = timed(capture(combine_only).replay, args.steps)[0] / (args.steps * len(layers))
+
+    # small-q sweep: q = 1..7 query tokens over the same KV, block tables and scales
+    small_q = {}
+    if not (args.no_sweep or args.no_extras) and nq == 8:
+        for qn in range(1, 8):
+            gen = torch.Generator(device="cuda")
+            gen.manual_seed(9000 + qn)
+            lq = [dataclasses.replace(inp, q=torch.randn((1, qn, 6, 256), generator=gen, device="cuda")
+                                      .to(torch.float16)) for inp in layers]
+            dq = dfv.desc_for(lq[0])
+            wq = [dfv.Workspace.allocate(dq) for _ in lq]
+
+            def step_q():
+                for inp, ws in zip(lq, wq):
+                    dfv.run_layer(inp, ws, dq)
+            for _ in range(args.warmup):
+                step_q()
+            small_q[f"q{qn}"] = round(timed(step_q, args.steps)[0] / args.steps, 4)
+            del lq, wq
+
+    # page-read ceiling: the same K and V pages in block-table order, no compute
+    probe = ctypes.CDLL(os.path.join(ROOT, "long_context_split_amd", "libdfv_probe.so"))
+    probe.dfv_probe_page_read.restype = ctypes.c_int
+    probe.dfv_probe_page_read.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                          ctypes.c_void_p, ctypes.c_void_p]
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    npages = -(-L // 16)
+
+    def probe_layers():
+        for inp in layers:
+            rc = probe.dfv_probe_page_read(inp.k_cache.data_ptr(), inp.v_cache.data_ptr(),
+                                           inp.block_table.data_ptr(), npages, sink.data_ptr(),
+                                           torch.cuda.current_stream().cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"page-read probe failed ({rc})")
+    probe_ms = None
+    if not args.no_extras:
+        for _ in range(args.warmup):
+            probe_layers()
+        probe_ms = timed(probe_layers, args.steps)[0] / (args.steps * len(layers))
 
     kv_bytes_layer = 2 * L * 256          # K + V E4M3 bytes per layer: 512 B per context token
     nrows = nq * 6
     ws_bytes = nrows * 80 * (256 + 2) * 4
     all_bytes_layer = kv_bytes_layer + nrows * 256 * 2 + (-(-L // 16)) * 4 + 2 * ws_bytes + nrows * 256 * 2
     achieved = kv_bytes_layer / (kernel_ms * 1e-3) / 1e9
+    ceiling = kv_bytes_layer / (probe_ms * 1e-3) / 1e9 if probe_ms else None
     traffic = measured_traffic(kv_bytes_layer)
 
     line = {
@@ -183,17 +249,29 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "layers": len(layers), "context": L, "num_q": nq,
                    "q_heads": 6, "kv_heads": 1, "head_dim": 256, "page_tokens": 16, "splits": 80,
-                   "timing": "hip graph replay" if graph else "stream launches"},
+                   "timing": "hip graph replay" if args.graph else "stream launches"},
+        "step_ms_median": round(q50, 4),
+        "step_ms_p10": round(q10, 4),
+        "step_ms_p90": round(q90, 4),
+        "stream_ms_per_step": round(stream_total / args.steps, 4),
+        "graph_ms_per_step": round(graph_total / args.steps, 4) if graph_total else None,
         "kv_GBps_whole_step": round(kv_bytes_layer * len(layers) / (ms_per_step * 1e-3) / 1e9, 1),
         "all_bytes_GBps_whole_step": round(all_bytes_layer * len(layers) / (ms_per_step * 1e-3) / 1e9, 1),
         "split_kernel_ms_per_launch": round(kernel_ms, 5),
-        "split_stage_ms_per_call": round(split_ms, 5),
+        "split_stage_ms_per_call": round(split_ms, 5) if split_ms else None,
+        "combine_ms_per_call": round(combine_ms, 5) if combine_ms else None,
         "key_chunks_per_split": dfv.chunks(desc),
+        "small_q_ms_per_step": small_q or None,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,
                      "kernel": "split_kernel",
                      "algorithmic_bytes_per_launch": kv_bytes_layer},
+        "page_read_ceiling": {"GBps": round(ceiling, 1), "us_per_layer": round(probe_ms * 1000, 2),
+                              "frac_of_peak": round(ceiling / HBM_PEAK_GBPS, 4),
+                              "split_kernel_frac_of_ceiling": round(achieved / ceiling, 4),
+                              "what": "the layer's K and V pages in block-table order through LDS, "
+                                      "no compute (libdfv_probe.so)"} if ceiling else None,
     }
     if args.calibrate_copy:
         src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")

@@ -17,6 +17,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libdfv.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
+# measurement probe (page-read ceiling), loaded only by the benchmark
+PROBE_NAME = "libdfv_probe.so"
+PROBE_PATH = os.path.join(PKG, PROBE_NAME)
+PROBE_SOURCES = ["probe_kernel.hip"]
 ARCH = "gfx950"
 
 SOURCES = ["split_kernel.hip", "combine_kernel.hip", "dfv_api.cpp"]
@@ -40,23 +44,28 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source for gfx950 and link the shared library; returns its path."""
+def _link(sources, exports, out_path, verbose):
     with tempfile.TemporaryDirectory() as tmp:
         vs = os.path.join(tmp, "exports.map")
         with open(vs, "w") as f:
-            f.write("{ global: dfv_*; local: *; };\n")
-        out_tmp = os.path.join(tmp, LIB_NAME)
+            f.write("{ global: %s; local: *; };\n" % exports)
+        out_tmp = os.path.join(tmp, os.path.basename(out_path))
         cmd = [hipcc(), *HIPCC_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}",
-               *[os.path.join(CSRC, s) for s in SOURCES],
+               *[os.path.join(CSRC, s) for s in sources],
                f"-Wl,--version-script={vs}", "-o", out_tmp]
         if verbose:
             print(" ".join(cmd), flush=True)
         res = subprocess.run(cmd, capture_output=True, text=True)
         if res.returncode != 0:
             sys.stderr.write(res.stdout + res.stderr)
-            raise RuntimeError("hipcc failed building libdfv.so")
-        shutil.move(out_tmp, LIB_PATH)
+            raise RuntimeError(f"hipcc failed building {os.path.basename(out_path)}")
+        shutil.move(out_tmp, out_path)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source for gfx950 and link the libraries; returns the path of libdfv.so."""
+    _link(SOURCES, "dfv_*", LIB_PATH, verbose)
+    _link(PROBE_SOURCES, "dfv_probe_*", PROBE_PATH, verbose)
     return LIB_PATH
 
 
