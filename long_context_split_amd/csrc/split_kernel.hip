@@ -212,24 +212,54 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
   const int b = grp / NS;
   const int jsp = grp % NS;
 
+  // The chunk's 32-key tiles [t_lo, t_hi) for a context of L keys.
+  auto chunk_tiles = [&](int L, int& t_lo, int& t_hi) {
+    const int S = split_size_of(L, NS, a.split_tokens);
+    const int Tb = (L + kTile - 1) / kTile;
+    const int s_lo = min(jsp * (S / kTile), Tb);
+    const int s_hi = min((jsp + 1) * (S / kTile), Tb);
+    const int ns32 = s_hi - s_lo;
+    t_lo = s_lo + (chunk * ns32) / C;
+    t_hi = s_lo + ((chunk + 1) * ns32) / C;
+  };
+  // Block-table window k of page slot `wave` (one dword per lane: the page of
+  // 64-key tile 64k + lane, or the chunk's first page past the chunk), landing
+  // in g_pages[k & 1][wave] by direct-to-LDS load.
+  const int32_t* bt = block_table + (size_t)b * a.max_blocks;
+  auto window_dma = [&](int k, int plo, int pend, int nu_) {
+    const int tu = 64 * k + lane;
+    const int e = (tu < nu_ && plo + 4 * tu + wave < pend) ? plo + 4 * tu + wave : plo;
+    lds_dma4(bt, (unsigned)e * 4u, (LDS_AS void*)&g_pages[k & 1][wave][0]);
+  };
+  // The PV waves fetch the first windows before the context length is known,
+  // for the chunk that a context of max_context_len keys would give (entries
+  // below 16 * max_blocks, so always in bounds).  Once the length arrives the
+  // windows are kept if the chunk's pages are the same (a single sequence at
+  // its bound, or a fixed split size whose chunk lies below the true length)
+  // and fetched again otherwise.  This takes one memory latency off the start.
+  int spec_lo = 0, spec_end = 0, spec_nu = 0;
+  if (!scorer) {
+    int tl, th;
+    chunk_tiles(a.max_context_len, tl, th);
+    spec_lo = 2 * tl;
+    spec_end = min(2 * th, (a.max_context_len + kPage - 1) / kPage);
+    spec_nu = (th - tl + 1) / 2;
+    if (spec_nu > 0) window_dma(0, spec_lo, spec_end, spec_nu);
+    if (spec_nu > 64) window_dma(1, spec_lo, spec_end, spec_nu);
+  }
+
   const float c = a.softmax_scale * k_scale[0];
   const float c2 = c * kLog2e;
   const float ofac = v_scale[0] * (1.0f / kPScale);
   const int L = clamp_len(context_lens[b], NQ, a.max_context_len);
-  const int S = split_size_of(L, NS, a.split_tokens);
-  const int Tb = (L + kTile - 1) / kTile;
-  const int s_lo = min(jsp * (S / kTile), Tb);
-  const int s_hi = min((jsp + 1) * (S / kTile), Tb);
-  const int ns32 = s_hi - s_lo;
-  const int t_lo = s_lo + (chunk * ns32) / C;          // chunk = 32-key tiles [t_lo, t_hi)
-  const int t_hi = s_lo + ((chunk + 1) * ns32) / C;
+  int t_lo, t_hi;                                      // chunk = 32-key tiles [t_lo, t_hi)
+  chunk_tiles(L, t_lo, t_hi);
   const int npages = (L + kPage - 1) / kPage;
   const int page_lo = 2 * t_lo;
   const int page_end = min(2 * t_hi, npages);          // pages of the chunk that exist
   const int key_lo = kTile * t_lo;
   const int key_end = min(kTile * t_hi, L);            // keys of the chunk
   const int nu = (t_hi - t_lo + 1) / 2;                // 64-key tiles
-  const int32_t* bt = block_table + (size_t)b * a.max_blocks;
 
   auto stage_of = [&](int t) { return (LDS_AS uint8_t*)g_ring + (t % kStages) * kTileBytes; };
 
@@ -262,11 +292,7 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
   // load sits between a tile's turn and its DMA; the block table is never read
   // any other way.  Lanes past the chunk read a valid entry whose value is
   // never used.
-  auto load_window = [&](int k) {
-    const int tu = 64 * k + lane;
-    const int e = (tu < nu && page_lo + 4 * tu + wave < page_end) ? page_lo + 4 * tu + wave : page_lo;
-    lds_dma4(bt, (unsigned)e * 4u, (LDS_AS void*)&g_pages[k & 1][wave][0]);
-  };
+  auto load_window = [&](int k) { window_dma(k, page_lo, page_end, nu); };
   auto issue_tile = [&](int u, int pg) { issue_page(u, __builtin_amdgcn_readlane(pg, u & 63)); };
   // This wave's LDS loads still allowed in flight once tile u has landed, when
   // tiles u+1..u+ahead have been issued after it.
@@ -477,17 +503,21 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
   // rows past 6q repeat the last real row.
   LDS_AS uint8_t* const qstage = (LDS_AS uint8_t*)&g_p[0][0];
   static_assert(sizeof(g_p) >= kMaxRB * 8 * 1024, "Q staging fits in the P buffers");
-  // PV waves: windows 0 and 1, then tiles 0..kStages-1.
-  auto start_stream = [&]() {
-    if (nu > 0) load_window(0);
-    if (nu > 64) load_window(1);
+  // PV waves: windows 0 and 1 (unless the speculative ones hold the same
+  // pages), then tiles 0..kStages-1.
+  auto start_stream = [&](bool spec_ok) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (!spec_ok) {
+      if (nu > 0) load_window(0);
+      if (nu > 64) load_window(1);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
     pg = g_pages[0][wave][lane];
 #pragma unroll
     for (int u = 0; u < kStages; ++u) issue_tile(u, pg);
   };
   if (!scorer) {
-    start_stream();
+    start_stream(spec_lo == page_lo && spec_end == page_end && spec_nu == nu);
     wait_dma(pending_after(0, kStages - 1));   // tile 0 (the score waves read it after the barrier)
   } else {
     const _Float16* qb = q + (size_t)b * ROWS * kHeadDim;
@@ -654,7 +684,7 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) o[mb][rb] = float4v{0.f, 0.f, 0.f, 0.f};
-      start_stream();
+      start_stream(false);
       wait_dma(pending_after(0, kStages - 1));
       __syncthreads();   // restart: tile 0 landed
       wait_dma(pending_after(1, kStages - 2));
