@@ -17,13 +17,16 @@ Modules:
 * :mod:`oracle.e4m3`      -- OCP E4M3 decode table built from the format's formula.
 * :mod:`oracle.attention` -- unsplit softmax attention, the 80 per-split FP64
   (max, sum, numerator) states and their merge.
+* :mod:`oracle.qk`        -- the QK stage on its own: every FP32 tiled score with
+  its masks and the untouched guard region ([#589] Purpose, Test Plan).
 * :mod:`oracle.brute`     -- a pure-Python brute force for tiny inputs, used to pin
-  :mod:`oracle.attention`.
+  :mod:`oracle.attention` and :mod:`oracle.qk`.
 
 Pins (all in ``tests/``, CPU only): the decode table against torch's
 ``float8_e4m3fn`` cast and OCP spec values; the attention against the brute
 force, split-count invariance, closed forms (equal keys, equal values, one key)
 and paging invariance; the split-size rule against the pages' split of 3296
-tokens at the 261888-token capacity boundary.  No function here is
+tokens at the 261888-token capacity boundary; the tiled scores against the
+brute force, a closed form, the attention oracle and paging invariance.  No function here is
 "parity unpinned".
 """

@@ -93,3 +93,38 @@ def brute_force(q, k_cache, v_cache, block_table, context_lens, k_scale, v_scale
         ls.append(lb)
         os_.append(obb)
     return outs, ms, ls, os_
+
+
+def brute_scores(q, k_cache, block_table, context_lens, k_scale, softmax_scale, ld: int, tile: int = 32):
+    """Scores as nested lists [b][r][t], r = 6i + h, for the QK-stage pins.
+
+    Exact rational dot products rounded once, token by token through the
+    block table; a written 32-key tile holds -inf where the row must not look
+    (t > p_i or t >= L_b); positions past the last written tile are NaN.
+    """
+    B, nq, hq, d = q.shape
+    hkv = k_cache.shape[2]
+    group = hq // hkv
+    c = Fraction(float(np.float32(softmax_scale))) * Fraction(float(np.float32(k_scale)))
+    out = []
+    for b in range(B):
+        L = int(context_lens[b])
+        end = tile * ((L + tile - 1) // tile)
+        rows_b = []
+        for i in range(nq):
+            p_i = L - nq + i
+            for h in range(hq):
+                kvh = h // group
+                qv = [Fraction(float(x)) for x in q[b, i, h, :].tolist()]
+                row = []
+                for t in range(ld):
+                    if t >= end:
+                        row.append(math.nan)
+                    elif t > p_i:
+                        row.append(-math.inf)
+                    else:
+                        kr = _token_row(k_cache, block_table[b], t, kvh)
+                        row.append(float(c * sum(qv[e] * Fraction(kr[e]) for e in range(d))))
+                rows_b.append(row)
+        out.append(rows_b)
+    return out
