@@ -185,6 +185,23 @@ DFV_API dfv_status dfv_attn(const dfv_attn_desc* desc, const void* q, const uint
                     float* ws_max, float* ws_sum, float* ws_num, void* scratch,
                     size_t scratch_bytes, void* out, void* stream);
 
+/* QK stage on its own ([#589] Purpose: the QK producer the pages time by
+ * itself, without softmax, PV or the split merge; [#589] Test Plan: checked
+ * score by score and guard tile by guard tile before timing).  Writes
+ *   scores[b][r][t] = c * <Q[b, i, h, :], K_t>,   r = 6i + h,
+ * FP32, for every 32-key tile that starts inside the context (t < 32 *
+ * ceil(L_b / 32)), with -inf where row r must not look (t > p_i, which covers
+ * t >= L_b).  Positions from 32 * ceil(L_b / 32) up to ld are never written
+ * (the guard region keeps the caller's contents).  Layout float32[B][6q][ld];
+ * ld must be a multiple of 32 and at least 32 * ceil(max_context_len / 32).
+ * The descriptor is validated as for the other calls; its split fields are not
+ * used.  v_cache, v_scale and the workspace play no part.
+ * Alignment: q, k_cache, scores 16 bytes; block_table, context_lens, k_scale
+ * 4 bytes. */
+DFV_API dfv_status dfv_qk_scores(const dfv_attn_desc* desc, const void* q, const uint8_t* k_cache,
+                                 const int32_t* block_table, const int32_t* context_lens,
+                                 const float* k_scale, float* scores, int64_t ld, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

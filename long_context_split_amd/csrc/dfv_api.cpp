@@ -10,6 +10,7 @@
 #include <math.h>
 
 #include "dfv_common.h"
+#include "dfv_qk.h"
 
 namespace {
 
@@ -219,6 +220,33 @@ dfv_status dfv_attn(const dfv_attn_desc* desc, const void* q, const uint8_t* k_c
                            ws_max, ws_sum, ws_num, cs, (hipStream_t)stream);
   if (s != DFV_OK) return s;
   return launch_combine_checked(desc, cs, ws_max, ws_sum, ws_num, out, (hipStream_t)stream);
+}
+
+dfv_status dfv_qk_scores(const dfv_attn_desc* desc, const void* q, const uint8_t* k_cache,
+                         const int32_t* block_table, const int32_t* context_lens, const float* k_scale,
+                         float* scores, int64_t ld, void* stream) {
+  dfv_status s = check_desc(desc);
+  if (s != DFV_OK) return s;
+  if (!q || !k_cache || !block_table || !context_lens || !k_scale || !scores) return DFV_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(scores, 16) || !aligned(block_table, 4) ||
+      !aligned(context_lens, 4) || !aligned(k_scale, 4))
+    return DFV_ERR_ALIGN;
+  const long long tiles = (desc->max_context_len + dfv::kTile - 1) / dfv::kTile;
+  if (ld % dfv::kTile != 0 || ld < tiles * dfv::kTile) return DFV_ERR_ARG;
+  dfv::QkArgs a;
+  a.q = (const _Float16*)q;
+  a.k_cache = k_cache;
+  a.block_table = block_table;
+  a.context_lens = context_lens;
+  a.k_scale = k_scale;
+  a.scores = scores;
+  a.ld = ld;
+  a.batch = desc->batch;
+  a.num_q = desc->num_q;
+  a.max_blocks = desc->max_blocks_per_seq;
+  a.max_context_len = desc->max_context_len;
+  a.softmax_scale = desc->softmax_scale;
+  return dfv::launch_qk(a, (hipStream_t)stream) == hipSuccess ? DFV_OK : DFV_ERR_LAUNCH;
 }
 
 }  // extern "C"

@@ -18,7 +18,7 @@ DFV_OK = 0
 STATUS = {0: "DFV_OK", -1: "DFV_ERR_NULL", -2: "DFV_ERR_UNSUPPORTED", -3: "DFV_ERR_ALIGN",
           -4: "DFV_ERR_ARG", -5: "DFV_ERR_LAUNCH", -7: "DFV_ERR_SCRATCH"}
 ENTRY_POINTS = ("dfv_status_string", "dfv_attn_check", "dfv_attn_scratch_bytes", "dfv_attn_chunks",
-                "dfv_attn_split_chunks", "dfv_attn_split", "dfv_attn_combine", "dfv_attn")
+                "dfv_attn_split_chunks", "dfv_attn_split", "dfv_attn_combine", "dfv_attn", "dfv_qk_scores")
 
 
 class DfvError(RuntimeError):
@@ -63,6 +63,8 @@ def lib():
         L.dfv_attn_combine.restype = ctypes.c_int
         L.dfv_attn.argtypes = [ctypes.POINTER(Desc)] + [_P] * 10 + [_P, ctypes.c_size_t, _P, _P]
         L.dfv_attn.restype = ctypes.c_int
+        L.dfv_qk_scores.argtypes = [ctypes.POINTER(Desc)] + [_P] * 6 + [ctypes.c_int64, _P]
+        L.dfv_qk_scores.restype = ctypes.c_int
         _LIB = L
     return _LIB
 
@@ -170,6 +172,18 @@ def attn(desc: Desc, q, k_cache, v_cache, block_table, context_lens, k_scale, v_
                         0 if scratch is None else scratch.numel() * scratch.element_size(),
                         _ptr(out), _stream(stream))
     _raise(st, "dfv_attn")
+
+
+def qk_ld(desc: Desc) -> int:
+    """Smallest admitted row stride of the QK-stage scores: 32 * ceil(max_context_len / 32)."""
+    return 32 * (-(-desc.max_context_len // 32))
+
+
+def qk_scores(desc: Desc, q, k_cache, block_table, context_lens, k_scale, scores, ld: int, stream=None):
+    """dfv_qk_scores: FP32 tiled scores [B][6q][ld] (guard region past the last tile untouched)."""
+    st = lib().dfv_qk_scores(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(block_table),
+                             _ptr(context_lens), _ptr(k_scale), _ptr(scores), int(ld), _stream(stream))
+    _raise(st, "dfv_qk_scores")
 
 
 def run_layer(inp, ws: Workspace, desc: Desc, stream=None):

@@ -82,3 +82,34 @@ def score_error_scale(q, k_cache, block_table, context_lens, k_scale, softmax_sc
             for h in range(hq):
                 out[b, i * hq + h, :L] = (k_abs[:, h // group, :] @ qb[i, h, :]) * c
     return out
+
+
+def scores_at(q, k_cache, block_table, context_lens, k_scale, softmax_scale, b: int, keys):
+    """FP64 scores [6q, len(keys)] of sequence b at the given key positions.
+
+    Same definition and masks as :func:`tiled_scores` (-inf where the row must
+    not look, NaN at guard positions), evaluated only where asked, so that
+    full-length contexts can be checked at sampled keys.
+    """
+    nq, hq, d = q.shape[1:]
+    hkv = k_cache.shape[2]
+    group = hq // hkv
+    c = float(np.float32(softmax_scale)) * float(np.float32(k_scale))
+    L = int(context_lens[b])
+    end = TILE_KEYS * (-(-L // TILE_KEYS))
+    keys = np.asarray(keys, dtype=np.int64)
+    pos = query_positions(L, nq)
+    out = np.full((nq * hq, keys.size), np.nan, dtype=np.float64)
+    inside = keys < L
+    block_size = k_cache.shape[1]
+    pages = np.asarray(block_table[b], dtype=np.int64)[keys[inside] // block_size]
+    k_hat = e4m3.decode(k_cache[pages, keys[inside] % block_size])          # [n, Hkv, D]
+    qb = q[b].astype(np.float64)
+    for i in range(nq):
+        for h in range(hq):
+            r = i * hq + h
+            row = np.full(keys.size, np.nan)
+            row[inside] = (k_hat[:, h // group, :] @ qb[i, h, :]) * c
+            row[(keys < end) & (keys > pos[i])] = -np.inf
+            out[r] = row
+    return out

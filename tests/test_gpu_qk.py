@@ -1,0 +1,141 @@
+"""QK stage on its own (dfv_qk_scores) vs the FP64 oracle, through the C ABI (GPU only).
+
+Every score of small cases (many 32-key tiles, ragged tails, several
+sequences, every q) is compared with the oracle; at full context length,
+sampled tiles are compared and the mask and guard structure is checked over
+the whole buffer.  The guard region past each sequence's last tile is filled
+with a canary bit pattern before the call and must still hold it afterwards.
+
+Tolerance: the kernel forms each score as an FP32-accumulated sum of 256
+exact FP16 x FP16 products, then multiplies by c in FP32.  For any summation
+order the error is at most 256 * 2^-24 * sum_d |Q_d K_d| (times c), plus one
+rounding of the product by c (2^-24 |s|) and of c itself (2^-24 |s|), so
+  |s_gpu - s_ref| <= 2^-16 * c * sum_d |Q_d K_d| + 2^-22 * |s_ref|.
+Masked positions must be exactly -inf and unmasked ones finite.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from long_context_split_amd import dfv, synth
+from oracle import qk as QK
+
+pytestmark = pytest.mark.gpu
+
+CANARY = np.int32(0x7FBADBAD)   # a NaN bit pattern no kernel result has
+
+
+def _note(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def _run(inp, ld=None):
+    desc = dfv.desc_for(inp)
+    ld = ld or dfv.qk_ld(desc)
+    B, nq = inp.q.shape[:2]
+    scores = torch.empty((B, 6 * nq, ld), dtype=torch.float32, device="cuda")
+    scores.view(torch.int32).fill_(int(CANARY))
+    dfv.qk_scores(desc, inp.q, inp.k_cache, inp.block_table, inp.context_lens, inp.k_scale, scores, ld)
+    torch.cuda.synchronize()
+    return scores, desc, ld
+
+
+def _check(got, ref, err):
+    """got float32 array; ref FP64 with -inf masks and NaN for guard positions; err = c*sum|qk|."""
+    bits = got.view(np.int32)
+    guard = np.isnan(ref)
+    assert np.all(bits[guard] == CANARY), "guard region written"
+    masked = np.isneginf(ref)
+    assert np.all(np.isneginf(got[masked])), "masked score not -inf"
+    vis = np.isfinite(ref)
+    assert np.all(np.isfinite(got[vis])), "visible score not finite"
+    d = np.abs(got[vis].astype(np.float64) - ref[vis])
+    tol = 2.0 ** -16 * err[vis] + 2.0 ** -22 * np.abs(ref[vis])
+    worst = float(np.max(d / np.maximum(tol, 1e-300))) if d.size else 0.0
+    assert worst <= 1.0, f"score error {worst:.3f} x tolerance"
+
+
+def _oracle(inp, ld):
+    d = inp.numpy()
+    a = (d["q"], d["k_cache"], d["block_table"], d["context_lens"], d["k_scale"], d["softmax_scale"])
+    return QK.tiled_scores(*a, ld=ld), QK.score_error_scale(*a, ld=ld)
+
+
+@pytest.mark.parametrize("lens,nq", [([4096], 8), ([1000], 8), ([777], 3), ([65], 1), ([8], 8),
+                                     ([3000, 1234], 5), ([33, 2049, 512], 2), ([16], 6), ([31], 7)])
+def test_every_score_matches_oracle(lens, nq):
+    _note(f"qk scores lens={lens} q={nq}")
+    inp = synth.make_layer(lens, nq, seed_base=5100 + nq + len(lens), device="cuda")
+    scores, desc, ld = _run(inp)
+    ref, err = _oracle(inp, ld)
+    _check(scores.cpu().numpy(), ref, err)
+
+
+def test_wider_stride_keeps_the_guard():
+    _note("qk scores with ld past the last tile")
+    inp = synth.make_layer([1000, 300], 4, seed_base=5201, device="cuda")
+    scores, desc, ld = _run(inp, ld=1024 + 96)
+    ref, err = _oracle(inp, ld)
+    _check(scores.cpu().numpy(), ref, err)
+
+
+def test_peaky_keys_scores():
+    _note("qk scores, peaky keys")
+    inp = synth.make_layer([5000], 8, seed_base=5301, device="cuda", key_mix=0.05)
+    scores, desc, ld = _run(inp)
+    ref, err = _oracle(inp, ld)
+    _check(scores.cpu().numpy(), ref, err)
+
+
+def test_deterministic_and_graph_capturable():
+    _note("qk scores: repeat and graph replay")
+    inp = synth.make_layer([4100, 900], 8, seed_base=5401, device="cuda")
+    s1, desc, ld = _run(inp)
+    s2, _, _ = _run(inp)
+    assert torch.equal(s1.view(torch.int32), s2.view(torch.int32))
+    out = torch.empty_like(s1)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dfv.qk_scores(desc, inp.q, inp.k_cache, inp.block_table, inp.context_lens, inp.k_scale, out, ld)
+    for _ in range(3):
+        out.view(torch.int32).fill_(int(CANARY))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int32), s1.view(torch.int32))
+
+
+@pytest.mark.parametrize("name,layer", [("ctx261888_16layer", 0), ("ctx131072_peaky_16layer", 5)])
+def test_full_size_sampled_tiles(name, layer):
+    _note(f"qk scores full size {name} layer {layer}")
+    inp = synth.workload_layer(name, layer, device="cuda")
+    scores, desc, ld = _run(inp)
+    got = scores.cpu().numpy()[0]
+    d = inp.numpy()
+    a = (d["q"], d["k_cache"], d["block_table"], d["context_lens"], d["k_scale"], d["softmax_scale"])
+    L = int(d["context_lens"][0])
+    nq = d["q"].shape[1]
+    T = -(-L // 32)
+    rng = np.random.default_rng(layer)
+    tiles = np.unique(np.concatenate([[0, 1, T - 2, T - 1], rng.integers(0, T, 60)]))
+    keys = (32 * tiles[:, None] + np.arange(32)[None, :]).ravel()
+    ref = QK.scores_at(*a, b=0, keys=keys)
+    # error scale at the sampled keys: |Q| . |K| (oracle decode, FP64)
+    qa = np.abs(d["q"][0].astype(np.float64)).reshape(6 * nq, -1)
+    err = np.zeros_like(ref)
+    inside = keys < L
+    kpages = d["block_table"][0][keys[inside] // 16]
+    from oracle import e4m3
+    kabs = np.abs(e4m3.decode(d["k_cache"][kpages, keys[inside] % 16, 0, :]))
+    c = float(np.float32(d["softmax_scale"])) * float(np.float32(d["k_scale"]))
+    err[:, inside] = (qa @ kabs.T) * c
+    _check(got[:, keys], ref, err)
+    # Structure over the whole buffer: row r = 6i + h sees keys 0..L-q+i, -inf up to the tile end.
+    for r in range(6 * nq):
+        lim = L - nq + r // 6
+        assert np.all(np.isfinite(got[r, :lim + 1]))
+        assert np.all(np.isneginf(got[r, lim + 1:32 * T]))
+    assert np.all(got[:, 32 * T:].view(np.int32) == CANARY)

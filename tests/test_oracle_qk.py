@@ -168,3 +168,12 @@ def test_qk_catches_wrong_row_order(monkeypatch):
         return s.reshape(B, nq, 6, ld).transpose(0, 2, 1, 3).reshape(B, R, ld)
     monkeypatch.setattr(QK, "tiled_scores", heads_major)
     assert _disagrees()
+
+
+def test_scores_at_agrees_with_tiled_scores():
+    dat = layer_np([70, 45], 3, seed=55, head_dim=16)
+    a = _qk_args(dat)
+    full = QK.tiled_scores(*a, ld=128)
+    keys = np.array([0, 1, 31, 32, 44, 45, 63, 64, 69, 70, 95, 96, 127])
+    for b in range(2):
+        assert _same(QK.scores_at(*a, b=b, keys=keys), full[b][:, keys], rtol=0.0)
