@@ -225,8 +225,25 @@ def main():
             probe_layers()
         probe_ms = timed(probe_layers, args.steps)[0] / (args.steps * len(layers))
 
+    # QK stage on its own: every FP32 tiled score of every layer (16 distinct
+    # score buffers, like the 16 layers' KV)
+    qk_ms = None
+    qk_tiles = dfv.qk_tiles(desc)
+    if not args.no_extras:
+        sbufs = [torch.empty((1, qk_tiles, nq * 6, 32), dtype=torch.float32, device="cuda") for _ in layers]
+
+        def qk_only():
+            for inp, sb in zip(layers, sbufs):
+                dfv.qk_scores(desc, inp.q, inp.k_cache, inp.block_table, inp.context_lens, inp.k_scale,
+                              sb, qk_tiles)
+        for _ in range(args.warmup):
+            qk_only()
+        qk_ms = timed(qk_only, args.steps)[0] / (args.steps * len(layers))
+        del sbufs
+
     kv_bytes_layer = 2 * L * 256          # K + V E4M3 bytes per layer: 512 B per context token
     nrows = nq * 6
+    qk_bytes_layer = L * 256 + nrows * 32 * qk_tiles * 4 + nrows * 256 * 2   # K in, scores out, Q in
     ws_bytes = nrows * 80 * (256 + 2) * 4
     all_bytes_layer = kv_bytes_layer + nrows * 256 * 2 + (-(-L // 16)) * 4 + 2 * ws_bytes + nrows * 256 * 2
     achieved = kv_bytes_layer / (kernel_ms * 1e-3) / 1e9
@@ -267,6 +284,12 @@ def main():
                      "traffic": traffic,
                      "kernel": "split_kernel",
                      "algorithmic_bytes_per_launch": kv_bytes_layer},
+        "qk_stage": {"us_per_launch": round(qk_ms * 1000, 2), "ms_per_16_layers": round(qk_ms * 16, 4),
+                     "GBps": round(qk_bytes_layer / (qk_ms * 1e-3) / 1e9, 1),
+                     "frac_of_peak": round(qk_bytes_layer / (qk_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                     "bytes_per_launch": qk_bytes_layer,
+                     "what": "dfv_qk_scores alone: the layer's K pages in, every FP32 tiled score out"}
+        if qk_ms else None,
         "page_read_ceiling": {"GBps": round(ceiling, 1), "us_per_layer": round(probe_ms * 1000, 2),
                               "frac_of_peak": round(ceiling / HBM_PEAK_GBPS, 4),
                               "split_kernel_frac_of_ceiling": round(achieved / ceiling, 4),

@@ -187,20 +187,22 @@ DFV_API dfv_status dfv_attn(const dfv_attn_desc* desc, const void* q, const uint
 
 /* QK stage on its own ([#589] Purpose: the QK producer the pages time by
  * itself, without softmax, PV or the split merge; [#589] Test Plan: checked
- * score by score and guard tile by guard tile before timing).  Writes
- *   scores[b][r][t] = c * <Q[b, i, h, :], K_t>,   r = 6i + h,
- * FP32, for every 32-key tile that starts inside the context (t < 32 *
- * ceil(L_b / 32)), with -inf where row r must not look (t > p_i, which covers
- * t >= L_b).  Positions from 32 * ceil(L_b / 32) up to ld are never written
- * (the guard region keeps the caller's contents).  Layout float32[B][6q][ld];
- * ld must be a multiple of 32 and at least 32 * ceil(max_context_len / 32).
+ * score by score and guard tile by guard tile before timing).  Computes
+ *   s[b][r][t] = c * <Q[b, i, h, :], K_t>,   r = 6i + h,
+ * in FP32 for whole 32-key tiles, stored tile-major:
+ *   scores float32[B][tiles_per_seq][6q][32],  s[b][r][t] at [b][t/32][r][t%32].
+ * Tile u of sequence b is written when it starts inside the context (u <
+ * ceil(L_b / 32)); inside it, -inf where row r must not look (t > p_i, which
+ * covers t >= L_b).  Tiles u >= ceil(L_b / 32) are guard tiles: never written,
+ * they keep the caller's contents.  tiles_per_seq >= ceil(max_context_len / 32).
  * The descriptor is validated as for the other calls; its split fields are not
  * used.  v_cache, v_scale and the workspace play no part.
  * Alignment: q, k_cache, scores 16 bytes; block_table, context_lens, k_scale
  * 4 bytes. */
 DFV_API dfv_status dfv_qk_scores(const dfv_attn_desc* desc, const void* q, const uint8_t* k_cache,
                                  const int32_t* block_table, const int32_t* context_lens,
-                                 const float* k_scale, float* scores, int64_t ld, void* stream);
+                                 const float* k_scale, float* scores, int64_t tiles_per_seq,
+                                 void* stream);
 
 #ifdef __cplusplus
 }

@@ -224,7 +224,7 @@ dfv_status dfv_attn(const dfv_attn_desc* desc, const void* q, const uint8_t* k_c
 
 dfv_status dfv_qk_scores(const dfv_attn_desc* desc, const void* q, const uint8_t* k_cache,
                          const int32_t* block_table, const int32_t* context_lens, const float* k_scale,
-                         float* scores, int64_t ld, void* stream) {
+                         float* scores, int64_t tiles_per_seq, void* stream) {
   dfv_status s = check_desc(desc);
   if (s != DFV_OK) return s;
   if (!q || !k_cache || !block_table || !context_lens || !k_scale || !scores) return DFV_ERR_NULL;
@@ -232,7 +232,7 @@ dfv_status dfv_qk_scores(const dfv_attn_desc* desc, const void* q, const uint8_t
       !aligned(context_lens, 4) || !aligned(k_scale, 4))
     return DFV_ERR_ALIGN;
   const long long tiles = (desc->max_context_len + dfv::kTile - 1) / dfv::kTile;
-  if (ld % dfv::kTile != 0 || ld < tiles * dfv::kTile) return DFV_ERR_ARG;
+  if (tiles_per_seq < tiles) return DFV_ERR_ARG;
   dfv::QkArgs a;
   a.q = (const _Float16*)q;
   a.k_cache = k_cache;
@@ -240,7 +240,7 @@ dfv_status dfv_qk_scores(const dfv_attn_desc* desc, const void* q, const uint8_t
   a.context_lens = context_lens;
   a.k_scale = k_scale;
   a.scores = scores;
-  a.ld = ld;
+  a.tiles_per_seq = tiles_per_seq;
   a.batch = desc->batch;
   a.num_q = desc->num_q;
   a.max_blocks = desc->max_blocks_per_seq;

@@ -12,8 +12,8 @@ struct QkArgs {
   const int32_t* block_table;  // [B][max_blocks]
   const int32_t* context_lens; // [B]
   const float* k_scale;        // device scalar
-  float* scores;               // [B][6q][ld]
-  long long ld;                // row stride in floats, a multiple of 32
+  float* scores;               // [B][tiles_per_seq][6q][32]
+  long long tiles_per_seq;     // tile capacity per sequence, >= ceil(max_context_len / 32)
   int batch;
   int num_q;
   int max_blocks;

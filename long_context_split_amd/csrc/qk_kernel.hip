@@ -7,11 +7,12 @@
 // What one launch computes: every FP32 score
 //   s[b][r][t] = c * <Q[b, i, h, :], K_t>,   r = 6i + h,   c = softmax_scale * k_scale,
 // with K_t the E4M3-decoded key row of token t read through the block table,
-// in whole 32-key tiles (the update tile of [#587] Implementation).  A tile is
-// written when it starts inside the context; inside it, keys that row r must
-// not see (t > p_i = L_b - q + i, which covers t >= L_b) hold -inf.  Nothing
-// is written from 32 * ceil(L_b / 32) on: that guard region keeps whatever the
-// caller put there.  This is the QK producer that the pages time and check by
+// in whole 32-key tiles (the update tile of [#587] Implementation), stored
+// tile-major: tile u of sequence b is one contiguous [6q][32] block.  A tile
+// is written when it starts inside the context; inside it, keys that row r
+// must not see (t > p_i = L_b - q + i, which covers t >= L_b) hold -inf.
+// Tiles from ceil(L_b / 32) on are guard tiles: never written, they keep
+// whatever the caller put there.  This is the QK producer that the pages time and check by
 // itself, score by score and guard tile by guard tile ([#589] Purpose, Test
 // Plan); as there, one decoded K fragment feeds the products of all three
 // 16-row blocks.
@@ -31,8 +32,9 @@
 //     through LDS) in registers; E4M3 is decoded with v_cvt_scalef32_pk_f16_fp8
 //     (exact in FP16), the per-tensor scale folded into c.
 //   * Each lane ends with 4 consecutive keys of one row per page; eight lanes
-//     cover a row's 32 keys, so every row of a tile leaves as one 128-byte
-//     line, with non-temporal stores (nothing in the launch reads it back).
+//     cover a row's 32 keys, and a tile's rows are adjacent, so a tile leaves
+//     as one contiguous 6q x 128-byte block, with non-temporal stores (nothing
+//     in the launch reads it back), one tile after it was computed.
 #include "dfv_qk.h"
 
 namespace dfv {
@@ -148,14 +150,29 @@ __global__ __launch_bounds__(kQkThreads) void qk_kernel(QkArgs a) {
   int limit[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) limit[rb] = L - NQ + min(16 * rb + n, ROWS - 1) / kQHeads;
-  float* const out_b = a.scores + (size_t)b * ROWS * a.ld;
+  float* const out_b = a.scores + (size_t)b * a.tiles_per_seq * ROWS * kTile;
 
+  // A tile's scores are stored one iteration later, after the wait for the
+  // next tile: on this GPU loads and stores share one counter and may complete
+  // out of order, so every wait is a full one, and a store issued just before
+  // it would make the wave wait for the store's round trip too.
+  float4v res[2][RB];
+  int res_t = -1;
+  auto store_res = [&]() {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int row = 16 * rb + n;
+      if (row >= ROWS) continue;
+      float* const dst = out_b + ((size_t)res_t * ROWS + row) * kTile + 4 * g;
+#pragma unroll
+      for (int p = 0; p < 2; ++p) __builtin_nontemporal_store(res[p][rb], (float4v*)(dst + 16 * p));
+    }
+  };
   issue(0);
   for (int k = 0; k < ntiles; ++k) {
-    // Tile k landed (and the previous tile's stores are done: on this GPU loads
-    // and stores share the counter and may complete out of order).
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // tile k landed; stores of tile k-2 done
     issue(k + 1);
+    if (res_t >= 0) store_res();
     const int t = t0 + k * W;
     const LDS_AS uint8_t* ks = (const LDS_AS uint8_t*)&g_qk_k[wave][k & 1][0] + n * 256;
     float4v sacc[2][RB];
@@ -180,23 +197,19 @@ __global__ __launch_bounds__(kQkThreads) void qk_kernel(QkArgs a) {
           sacc[p][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, qf[rb][2 * j + 1], sacc[p][rb], 0, 0, 0);
       }
     }
-    // Scale, mask (a page past the context was not loaded: its keys are all
-    // masked, whatever the slot held), store whole rows.
+    // Scale and mask (a page past the context was not loaded: its keys are all
+    // masked, whatever the slot held).
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const int row = 16 * rb + n;
-      if (row >= ROWS) continue;
-      float* const dst = out_b + (size_t)row * a.ld + kTile * t + 4 * g;
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
         const int key = kTile * t + 16 * p + 4 * g;
-        float4v v;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = (key + r <= limit[rb]) ? sacc[p][rb][r] * c : kNegInfQk;
-        __builtin_nontemporal_store(v, (float4v*)(dst + 16 * p));
+        for (int r = 0; r < 4; ++r) res[p][rb][r] = (key + r <= limit[rb]) ? sacc[p][rb][r] * c : kNegInfQk;
       }
-    }
+    res_t = t;
   }
+  if (res_t >= 0) store_res();
 }
 
 }  // namespace

@@ -174,15 +174,17 @@ def attn(desc: Desc, q, k_cache, v_cache, block_table, context_lens, k_scale, v_
     _raise(st, "dfv_attn")
 
 
-def qk_ld(desc: Desc) -> int:
-    """Smallest admitted row stride of the QK-stage scores: 32 * ceil(max_context_len / 32)."""
-    return 32 * (-(-desc.max_context_len // 32))
+def qk_tiles(desc: Desc) -> int:
+    """Smallest admitted tile capacity of the QK-stage scores: ceil(max_context_len / 32)."""
+    return -(-desc.max_context_len // 32)
 
 
-def qk_scores(desc: Desc, q, k_cache, block_table, context_lens, k_scale, scores, ld: int, stream=None):
-    """dfv_qk_scores: FP32 tiled scores [B][6q][ld] (guard region past the last tile untouched)."""
+def qk_scores(desc: Desc, q, k_cache, block_table, context_lens, k_scale, scores, tiles_per_seq: int,
+              stream=None):
+    """dfv_qk_scores: FP32 scores, tile-major [B][tiles_per_seq][6q][32]; guard tiles untouched."""
     st = lib().dfv_qk_scores(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(block_table),
-                             _ptr(context_lens), _ptr(k_scale), _ptr(scores), int(ld), _stream(stream))
+                             _ptr(context_lens), _ptr(k_scale), _ptr(scores), int(tiles_per_seq),
+                             _stream(stream))
     _raise(st, "dfv_qk_scores")
 
 

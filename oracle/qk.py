@@ -19,11 +19,12 @@ Readings taken here (the pages name the check but not the layout):
   Implementation).  A tile is written if it starts inside the context.  Inside
   a written tile, keys the row must not see (t > p_i, causal) and keys past the
   context (t >= L_b) hold -inf, as in the attention's masked softmax input.
-* The guard region is everything from the end of the last written tile,
-  32 * ceil(L_b / 32), to the row stride `ld`: nothing is written there.  This
-  function returns NaN at those positions, meaning "must still hold the
-  caller's canary".
-* Layout: scores[b][r][t], r = 6 i + h, row stride ld >= 32 * ceil(L_max / 32).
+* Guard tiles are the tiles from ceil(L_b / 32) on, up to the buffer's tile
+  capacity: nothing is written there.  The functions here return NaN at those
+  positions, meaning "must still hold the caller's canary".
+* Values are indexed logically as s[b][r][t] (r = 6 i + h) with a row length
+  ld = 32 * capacity; the buffer itself is tile-major, [b][t // 32][r][t % 32]
+  (each tile one contiguous block), which :func:`tile_major` produces.
 """
 from __future__ import annotations
 
@@ -113,3 +114,13 @@ def scores_at(q, k_cache, block_table, context_lens, k_scale, softmax_scale, b: 
             row[(keys < end) & (keys > pos[i])] = -np.inf
             out[r] = row
     return out
+
+
+def tile_major(s, tiles_per_seq: int):
+    """Rearrange logical scores [B, R, 32 * tiles_per_seq] into the buffer layout
+    [B, tiles_per_seq, R, 32] (element [b][u][r][x] is key 32u + x of row r).
+    A pure index permutation: no arithmetic."""
+    B, R, ld = s.shape
+    if ld != 32 * tiles_per_seq:
+        raise ValueError("logical row length must be 32 * tiles_per_seq")
+    return s.reshape(B, R, tiles_per_seq, 32).transpose(0, 2, 1, 3)

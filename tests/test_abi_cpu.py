@@ -154,18 +154,17 @@ def test_qk_scores_refuses_bad_arguments_before_launch(L):
     d = _good()
     P = ctypes.c_void_p
     ok = [P(4096 * (i + 1)) for i in range(6)]    # q, k_cache, block_table, context_lens, k_scale, scores
-    ld = 32 * (-(-d.max_context_len // 32))
+    tiles = -(-d.max_context_len // 32)
     bad = _good(head_dim=128)
-    assert L.dfv_qk_scores(ctypes.byref(bad), *ok, ld, None) == -2
+    assert L.dfv_qk_scores(ctypes.byref(bad), *ok, tiles, None) == -2
     args = list(ok)
     args[5] = None
-    assert L.dfv_qk_scores(ctypes.byref(d), *args, ld, None) == -1
+    assert L.dfv_qk_scores(ctypes.byref(d), *args, tiles, None) == -1
     args = list(ok)
     args[5] = P(4096 + 4)
-    assert L.dfv_qk_scores(ctypes.byref(d), *args, ld, None) == -3
+    assert L.dfv_qk_scores(ctypes.byref(d), *args, tiles, None) == -3
     args = list(ok)
     args[1] = P(4096 + 8)
-    assert L.dfv_qk_scores(ctypes.byref(d), *args, ld, None) == -3
-    assert L.dfv_qk_scores(ctypes.byref(d), *ok, ld - 32, None) == -4    # shorter than the last tile
-    assert L.dfv_qk_scores(ctypes.byref(d), *ok, ld + 16, None) == -4    # not a multiple of 32
-    assert dfv.qk_ld(d) == ld
+    assert L.dfv_qk_scores(ctypes.byref(d), *args, tiles, None) == -3
+    assert L.dfv_qk_scores(ctypes.byref(d), *ok, tiles - 1, None) == -4    # capacity below the last tile
+    assert dfv.qk_tiles(d) == tiles

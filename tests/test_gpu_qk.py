@@ -3,8 +3,9 @@
 Every score of small cases (many 32-key tiles, ragged tails, several
 sequences, every q) is compared with the oracle; at full context length,
 sampled tiles are compared and the mask and guard structure is checked over
-the whole buffer.  The guard region past each sequence's last tile is filled
-with a canary bit pattern before the call and must still hold it afterwards.
+the whole buffer.  The buffer is tile-major ([B][tile][6q][32]); the guard
+tiles past each sequence's last tile are filled with a canary bit pattern
+before the call and must still hold it afterwards.
 
 Tolerance: the kernel forms each score as an FP32-accumulated sum of 256
 exact FP16 x FP16 products, then multiplies by c in FP32.  For any summation
@@ -32,15 +33,17 @@ def _note(msg):
     sys.stdout.flush()
 
 
-def _run(inp, ld=None):
+def _run(inp, tiles=None):
+    """Scores in the logical [B][6q][32 * tiles] order (a view of the tile-major buffer)."""
     desc = dfv.desc_for(inp)
-    ld = ld or dfv.qk_ld(desc)
+    tiles = tiles or dfv.qk_tiles(desc)
     B, nq = inp.q.shape[:2]
-    scores = torch.empty((B, 6 * nq, ld), dtype=torch.float32, device="cuda")
-    scores.view(torch.int32).fill_(int(CANARY))
-    dfv.qk_scores(desc, inp.q, inp.k_cache, inp.block_table, inp.context_lens, inp.k_scale, scores, ld)
+    buf = torch.empty((B, tiles, 6 * nq, 32), dtype=torch.float32, device="cuda")
+    buf.view(torch.int32).fill_(int(CANARY))
+    dfv.qk_scores(desc, inp.q, inp.k_cache, inp.block_table, inp.context_lens, inp.k_scale, buf, tiles)
     torch.cuda.synchronize()
-    return scores, desc, ld
+    logical = buf.permute(0, 2, 1, 3).reshape(B, 6 * nq, 32 * tiles)
+    return logical, buf, desc, 32 * tiles
 
 
 def _check(got, ref, err):
@@ -69,15 +72,15 @@ def _oracle(inp, ld):
 def test_every_score_matches_oracle(lens, nq):
     _note(f"qk scores lens={lens} q={nq}")
     inp = synth.make_layer(lens, nq, seed_base=5100 + nq + len(lens), device="cuda")
-    scores, desc, ld = _run(inp)
+    scores, _, desc, ld = _run(inp)
     ref, err = _oracle(inp, ld)
     _check(scores.cpu().numpy(), ref, err)
 
 
-def test_wider_stride_keeps_the_guard():
-    _note("qk scores with ld past the last tile")
+def test_extra_capacity_keeps_the_guard_tiles():
+    _note("qk scores with capacity past the last tile")
     inp = synth.make_layer([1000, 300], 4, seed_base=5201, device="cuda")
-    scores, desc, ld = _run(inp, ld=1024 + 96)
+    scores, _, desc, ld = _run(inp, tiles=32 + 3)
     ref, err = _oracle(inp, ld)
     _check(scores.cpu().numpy(), ref, err)
 
@@ -85,7 +88,7 @@ def test_wider_stride_keeps_the_guard():
 def test_peaky_keys_scores():
     _note("qk scores, peaky keys")
     inp = synth.make_layer([5000], 8, seed_base=5301, device="cuda", key_mix=0.05)
-    scores, desc, ld = _run(inp)
+    scores, _, desc, ld = _run(inp)
     ref, err = _oracle(inp, ld)
     _check(scores.cpu().numpy(), ref, err)
 
@@ -93,26 +96,27 @@ def test_peaky_keys_scores():
 def test_deterministic_and_graph_capturable():
     _note("qk scores: repeat and graph replay")
     inp = synth.make_layer([4100, 900], 8, seed_base=5401, device="cuda")
-    s1, desc, ld = _run(inp)
-    s2, _, _ = _run(inp)
-    assert torch.equal(s1.view(torch.int32), s2.view(torch.int32))
-    out = torch.empty_like(s1)
+    _, b1, desc, _ = _run(inp)
+    _, b2, _, _ = _run(inp)
+    assert torch.equal(b1.view(torch.int32), b2.view(torch.int32))
+    out = torch.empty_like(b1)
+    tiles = b1.shape[1]
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        dfv.qk_scores(desc, inp.q, inp.k_cache, inp.block_table, inp.context_lens, inp.k_scale, out, ld)
+        dfv.qk_scores(desc, inp.q, inp.k_cache, inp.block_table, inp.context_lens, inp.k_scale, out, tiles)
     for _ in range(3):
         out.view(torch.int32).fill_(int(CANARY))
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        assert torch.equal(out.view(torch.int32), s1.view(torch.int32))
+        assert torch.equal(out.view(torch.int32), b1.view(torch.int32))
 
 
 @pytest.mark.parametrize("name,layer", [("ctx261888_16layer", 0), ("ctx131072_peaky_16layer", 5)])
 def test_full_size_sampled_tiles(name, layer):
     _note(f"qk scores full size {name} layer {layer}")
     inp = synth.workload_layer(name, layer, device="cuda")
-    scores, desc, ld = _run(inp)
+    scores, _, desc, ld = _run(inp)
     got = scores.cpu().numpy()[0]
     d = inp.numpy()
     a = (d["q"], d["k_cache"], d["block_table"], d["context_lens"], d["k_scale"], d["softmax_scale"])

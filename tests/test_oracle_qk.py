@@ -177,3 +177,15 @@ def test_scores_at_agrees_with_tiled_scores():
     keys = np.array([0, 1, 31, 32, 44, 45, 63, 64, 69, 70, 95, 96, 127])
     for b in range(2):
         assert _same(QK.scores_at(*a, b=b, keys=keys), full[b][:, keys], rtol=0.0)
+
+
+def test_tile_major_is_the_documented_index_map():
+    dat = layer_np([70], 2, seed=61, head_dim=16)
+    s = QK.tiled_scores(*_qk_args(dat), ld=96)
+    tm = QK.tile_major(s, 3)
+    assert tm.shape == (1, 3, 12, 32)
+    for u in range(3):
+        for r in range(12):
+            for x in (0, 5, 31):
+                a, b = tm[0, u, r, x], s[0, r, 32 * u + x]
+                assert (np.isnan(a) and np.isnan(b)) or a == b
