@@ -19,6 +19,8 @@ Modules:
   (max, sum, numerator) states and their merge.
 * :mod:`oracle.qk`        -- the QK stage on its own: every FP32 tiled score with
   its masks and the untouched guard region ([#589] Purpose, Test Plan).
+* :mod:`oracle.kv_append` -- E4M3 encoding (nearest, ties to even, saturating) of
+  new FP16 key/value rows and their write into the paged cache by slot.
 * :mod:`oracle.brute`     -- a pure-Python brute force for tiny inputs, used to pin
   :mod:`oracle.attention` and :mod:`oracle.qk`.
 
@@ -27,6 +29,9 @@ Pins (all in ``tests/``, CPU only): the decode table against torch's
 force, split-count invariance, closed forms (equal keys, equal values, one key)
 and paging invariance; the split-size rule against the pages' split of 3296
 tokens at the 261888-token capacity boundary; the tiled scores against the
-brute force, a closed form, the attention oracle and paging invariance.  No function here is
+brute force, a closed form, the attention oracle and paging invariance; the
+E4M3 encoder against torch's float8_e4m3fn cast wherever that cast is finite,
+an exhaustive round trip through the decode table, midpoint ties and the
+saturation reading.  No function here is
 "parity unpinned".
 """
