@@ -204,6 +204,26 @@ DFV_API dfv_status dfv_qk_scores(const dfv_attn_desc* desc, const void* q, const
                                  const float* k_scale, float* scores, int64_t tiles_per_seq,
                                  void* stream);
 
+/* Paged E4M3 KV append: writes the keys and values of num_tokens new tokens
+ * (the q verification tokens of each sequence) into the caches, the step that
+ * precedes the attention.  The pages keep the KV cache in E4M3 with per-tensor
+ * scales ([#589] Test Plan; [#556] Test Plan: E4M3 target KV) without stating
+ * the write; here every element is x / scale in FP32 (correctly rounded),
+ * saturated to +-448, rounded to the nearest E4M3 code (ties to even; NaN
+ * stays NaN) and stored at cache[slot / 16][slot % 16][0][d].
+ *   k_new, v_new   FP16  [num_tokens][1][256]
+ *   slot_mapping   int64 [num_tokens]; a slot outside [0, num_blocks * 16) is
+ *                  padding and writes nothing (device values are not checked
+ *                  on the host)
+ *   k_scale, v_scale  device FP32 scalars
+ *   k_cache, v_cache  uint8 [num_blocks][16][1][256]
+ * Tokens with equal slots race (the last writer is unspecified).  num_tokens =
+ * 0 launches nothing.  Alignment: k_new, v_new, k_cache, v_cache 16 bytes;
+ * slot_mapping 8 bytes; scales 4 bytes. */
+DFV_API dfv_status dfv_kv_append(const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                                 int32_t num_tokens, const float* k_scale, const float* v_scale,
+                                 uint8_t* k_cache, uint8_t* v_cache, int64_t num_blocks, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -10,6 +10,7 @@
 #include <math.h>
 
 #include "dfv_common.h"
+#include "dfv_append.h"
 #include "dfv_qk.h"
 
 namespace {
@@ -247,6 +248,29 @@ dfv_status dfv_qk_scores(const dfv_attn_desc* desc, const void* q, const uint8_t
   a.max_context_len = desc->max_context_len;
   a.softmax_scale = desc->softmax_scale;
   return dfv::launch_qk(a, (hipStream_t)stream) == hipSuccess ? DFV_OK : DFV_ERR_LAUNCH;
+}
+
+dfv_status dfv_kv_append(const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                         int32_t num_tokens, const float* k_scale, const float* v_scale,
+                         uint8_t* k_cache, uint8_t* v_cache, int64_t num_blocks, void* stream) {
+  if (num_tokens < 0 || num_blocks < 1 || num_blocks > (1LL << 40)) return DFV_ERR_ARG;
+  if (num_tokens > (1 << 28)) return DFV_ERR_ARG;
+  if (!k_new || !v_new || !slot_mapping || !k_scale || !v_scale || !k_cache || !v_cache)
+    return DFV_ERR_NULL;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(slot_mapping, 8) || !aligned(k_scale, 4) || !aligned(v_scale, 4))
+    return DFV_ERR_ALIGN;
+  dfv::AppendArgs a;
+  a.k_new = (const _Float16*)k_new;
+  a.v_new = (const _Float16*)v_new;
+  a.slot_mapping = slot_mapping;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.num_slots = num_blocks * dfv::kPage;
+  a.num_tokens = num_tokens;
+  return dfv::launch_kv_append(a, (hipStream_t)stream) == hipSuccess ? DFV_OK : DFV_ERR_LAUNCH;
 }
 
 }  // extern "C"

@@ -18,7 +18,8 @@ DFV_OK = 0
 STATUS = {0: "DFV_OK", -1: "DFV_ERR_NULL", -2: "DFV_ERR_UNSUPPORTED", -3: "DFV_ERR_ALIGN",
           -4: "DFV_ERR_ARG", -5: "DFV_ERR_LAUNCH", -7: "DFV_ERR_SCRATCH"}
 ENTRY_POINTS = ("dfv_status_string", "dfv_attn_check", "dfv_attn_scratch_bytes", "dfv_attn_chunks",
-                "dfv_attn_split_chunks", "dfv_attn_split", "dfv_attn_combine", "dfv_attn", "dfv_qk_scores")
+                "dfv_attn_split_chunks", "dfv_attn_split", "dfv_attn_combine", "dfv_attn", "dfv_qk_scores",
+                "dfv_kv_append")
 
 
 class DfvError(RuntimeError):
@@ -65,6 +66,8 @@ def lib():
         L.dfv_attn.restype = ctypes.c_int
         L.dfv_qk_scores.argtypes = [ctypes.POINTER(Desc)] + [_P] * 6 + [ctypes.c_int64, _P]
         L.dfv_qk_scores.restype = ctypes.c_int
+        L.dfv_kv_append.argtypes = [_P, _P, _P, ctypes.c_int32, _P, _P, _P, _P, ctypes.c_int64, _P]
+        L.dfv_kv_append.restype = ctypes.c_int
         _LIB = L
     return _LIB
 
@@ -186,6 +189,14 @@ def qk_scores(desc: Desc, q, k_cache, block_table, context_lens, k_scale, scores
                              _ptr(context_lens), _ptr(k_scale), _ptr(scores), int(tiles_per_seq),
                              _stream(stream))
     _raise(st, "dfv_qk_scores")
+
+
+def kv_append(k_new, v_new, slot_mapping, k_scale, v_scale, k_cache, v_cache, stream=None):
+    """dfv_kv_append: quantize new FP16 K/V rows to E4M3 and write them by slot (int64 slots)."""
+    st = lib().dfv_kv_append(_ptr(k_new), _ptr(v_new), _ptr(slot_mapping), int(slot_mapping.numel()),
+                             _ptr(k_scale), _ptr(v_scale), _ptr(k_cache), _ptr(v_cache),
+                             int(k_cache.shape[0]), _stream(stream))
+    _raise(st, "dfv_kv_append")
 
 
 def run_layer(inp, ws: Workspace, desc: Desc, stream=None):

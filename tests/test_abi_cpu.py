@@ -168,3 +168,20 @@ def test_qk_scores_refuses_bad_arguments_before_launch(L):
     assert L.dfv_qk_scores(ctypes.byref(d), *args, tiles, None) == -3
     assert L.dfv_qk_scores(ctypes.byref(d), *ok, tiles - 1, None) == -4    # capacity below the last tile
     assert dfv.qk_tiles(d) == tiles
+
+
+def test_kv_append_refuses_bad_arguments_before_launch(L):
+    P = ctypes.c_void_p
+    ok = dict(kn=P(4096), vn=P(8192), sl=P(12288), ks=P(16384), vs=P(16388), kc=P(1 << 20), vc=P(1 << 21))
+
+    def call(n=8, nb=64, **over):
+        a = dict(ok, **over)
+        return L.dfv_kv_append(a["kn"], a["vn"], a["sl"], n, a["ks"], a["vs"], a["kc"], a["vc"], nb, None)
+    assert call(n=-1) == -4
+    assert call(nb=0) == -4
+    assert call(kc=None) == -1
+    assert call(sl=None) == -1
+    assert call(kn=P(4096 + 2)) == -3
+    assert call(vc=P((1 << 21) + 4)) == -3
+    assert call(sl=P(12288 + 4)) == -3
+    assert call(n=0) == 0          # nothing to write: returns before any launch
