@@ -241,6 +241,29 @@ def main():
         qk_ms = timed(qk_only, args.steps)[0] / (args.steps * len(layers))
         del sbufs
 
+    # KV append of the q new tokens (last q positions of each layer's context),
+    # alone and followed by the attention: the whole verification pass.  Runs
+    # last among the GPU measurements because it rewrites those cache rows.
+    append_us = step_append_ms = None
+    if not args.no_extras:
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(777)
+        kn = [torch.randn((nq, 1, 256), generator=gen, device="cuda").to(torch.float16) for _ in layers]
+        vn = [torch.randn((nq, 1, 256), generator=gen, device="cuda").to(torch.float16) for _ in layers]
+        pos = torch.arange(L - nq, L, device="cuda")
+        slots = [(inp.block_table[0, pos // 16].to(torch.int64) * 16 + pos % 16).contiguous() for inp in layers]
+
+        def append_only():
+            for inp, a_k, a_v, sl in zip(layers, kn, vn, slots):
+                dfv.kv_append(a_k, a_v, sl, inp.k_scale, inp.v_scale, inp.k_cache, inp.v_cache)
+
+        def step_with_append():
+            for inp, ws, a_k, a_v, sl in zip(layers, wss, kn, vn, slots):
+                dfv.kv_append(a_k, a_v, sl, inp.k_scale, inp.v_scale, inp.k_cache, inp.v_cache)
+                dfv.run_layer(inp, ws, desc)
+        append_us = timed(capture(append_only).replay, args.steps)[0] / (args.steps * len(layers)) * 1000
+        step_append_ms = timed(capture(step_with_append).replay, args.steps)[0] / args.steps
+
     kv_bytes_layer = 2 * L * 256          # K + V E4M3 bytes per layer: 512 B per context token
     nrows = nq * 6
     qk_bytes_layer = L * 256 + nrows * 32 * qk_tiles * 4 + nrows * 256 * 2   # K in, scores out, Q in
@@ -284,6 +307,8 @@ def main():
                      "traffic": traffic,
                      "kernel": "split_kernel",
                      "algorithmic_bytes_per_launch": kv_bytes_layer},
+        "kv_append_us_per_call": round(append_us, 2) if append_us else None,
+        "graph_ms_per_step_with_kv_append": round(step_append_ms, 4) if step_append_ms else None,
         "qk_stage": {"us_per_launch": round(qk_ms * 1000, 2), "ms_per_16_layers": round(qk_ms * 16, 4),
                      "GBps": round(qk_bytes_layer / (qk_ms * 1e-3) / 1e9, 1),
                      "frac_of_peak": round(qk_bytes_layer / (qk_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
