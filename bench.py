@@ -185,6 +185,19 @@ def main():
         split_ms = timed(capture(split_only).replay, args.steps)[0] / (args.steps * len(layers))
         combine_ms = timed(capture(combine_only).replay, args.steps)[0] / (args.steps * len(layers))
 
+    # fixed-capacity graph: split size fixed at the capacity rule's 3296 tokens and
+    # the launch geometry taken from max_context_len, captured once; the
+    # device-side context lengths may change between replays (here they do not)
+    fixed_ms = None
+    if not (args.no_extras or args.no_sweep):
+        dfx = dfv.make_desc(1, nq, layers[0].block_table.shape[1], L, num_splits=80,
+                            split_tokens=32 * (-(-(-(-L // 80)) // 32)), softmax_scale=desc.softmax_scale)
+
+        def step_fixed():
+            for inp, ws in zip(layers, wss):
+                dfv.run_layer(inp, ws, dfx)
+        fixed_ms = timed(capture(step_fixed).replay, args.steps)[0] / args.steps
+
     # small-q sweep: q = 1..7 query tokens over the same KV, block tables and scales
     small_q = {}
     if not (args.no_sweep or args.no_extras) and nq == 8:
@@ -295,6 +308,7 @@ def main():
         "step_ms_p90": round(q90, 4),
         "stream_ms_per_step": round(stream_total / args.steps, 4),
         "graph_ms_per_step": round(graph_total / args.steps, 4) if graph_total else None,
+        "graph_ms_per_step_fixed_split_tokens": round(fixed_ms, 4) if fixed_ms else None,
         "kv_GBps_whole_step": round(kv_bytes_layer * len(layers) / (ms_per_step * 1e-3) / 1e9, 1),
         "all_bytes_GBps_whole_step": round(all_bytes_layer * len(layers) / (ms_per_step * 1e-3) / 1e9, 1),
         "split_kernel_ms_per_launch": round(kernel_ms, 5),
