@@ -86,13 +86,11 @@ __global__ __launch_bounds__(kQkThreads) void qk_kernel(QkArgs a) {
   const int b = blockIdx.x / gps;
   const int W = gps * kQkWaves;                      // waves per sequence
   const int t0 = (blockIdx.x % gps) * kQkWaves + wave;
-  const int L = min(max(a.context_lens[b], NQ), a.max_context_len);
-  const int Tb = (L + kTile - 1) / kTile;            // tiles written for this sequence
-  // At most kQkWindow by the launch geometry; the bound keeps every page-id
-  // read inside the window whatever the lengths.
-  const int ntiles = min(t0 < Tb ? (Tb - t0 + W - 1) / W : 0, kQkWindow);
-  const float c = a.softmax_scale * a.k_scale[0];
-
+  // The page ids are gathered for the tiles a context of max_context_len would
+  // have (entries below 16 * max_blocks, so in bounds), at the same time as the
+  // context length and Q arrive: no dependent load precedes the first DMA.
+  const int Tcap = (a.max_context_len + kTile - 1) / kTile;
+  const int ncap = min(t0 < Tcap ? (Tcap - t0 + W - 1) / W : 0, kQkWindow);
   // Q in MFMA B-operand order, staged once per workgroup: fragment f = rb*8 + m,
   // lane (n, g) holds Q[row 16rb + n][64g + 8m + 0..7]; rows past 6q repeat the
   // last real row (their scores are never stored).
@@ -105,20 +103,19 @@ __global__ __launch_bounds__(kQkThreads) void qk_kernel(QkArgs a) {
     }
   }
   // Page ids of this wave's tiles: lane j holds page j / 32 of tile j % 32
-  // (0 where the page lies past the context; such a page is never loaded).
+  // (0 past the capacity; a page past the context is never loaded).
   int page_v = 0;
   {
     const int k = lane & 31;
     const int pg = 2 * (t0 + k * W) + (lane >> 5);
-    if (k < ntiles && kPage * pg < L) page_v = a.block_table[(size_t)b * a.max_blocks + pg];
+    if (k < ncap && kPage * pg < a.max_context_len) page_v = a.block_table[(size_t)b * a.max_blocks + pg];
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  half8 qf[RB][8];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-    for (int m = 0; m < 8; ++m) qf[rb][m] = *(const LDS_AS half8*)(&g_qk_q[rb * 8 + m][lane * 16]);
+  const int L = min(max(a.context_lens[b], NQ), a.max_context_len);
+  const int Tb = (L + kTile - 1) / kTile;            // tiles written for this sequence
+  // At most kQkWindow by the launch geometry; the bound keeps every page-id
+  // read inside the window whatever the lengths.
+  const int ntiles = min(t0 < Tb ? (Tb - t0 + W - 1) / W : 0, kQkWindow);
+  const float c = a.softmax_scale * a.k_scale[0];
 
   // DMA lane offsets: load qq of page p fills LDS row r = 4qq + lane/16, chunk
   // position lane%16, with global chunk (lane%16) ^ r ^ 4p of that row.
@@ -145,6 +142,14 @@ __global__ __launch_bounds__(kQkThreads) void qk_kernel(QkArgs a) {
       for (int qq = 0; qq < 4; ++qq) lds_dma16_qk(p1, lane_off[1][qq], slot + kPageBytes + qq * 1024);
     }
   };
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // page ids (and this wave's Q fragments)
+  issue(0);                                           // the first tile goes out before the barrier
+  __syncthreads();                                    // every wave's Q fragments staged
+  half8 qf[RB][8];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int m = 0; m < 8; ++m) qf[rb][m] = *(const LDS_AS half8*)(&g_qk_q[rb * 8 + m][lane * 16]);
 
   // Causal bound of each of this lane's rows.
   int limit[RB];
@@ -168,7 +173,6 @@ __global__ __launch_bounds__(kQkThreads) void qk_kernel(QkArgs a) {
       for (int p = 0; p < 2; ++p) __builtin_nontemporal_store(res[p][rb], (float4v*)(dst + 16 * p));
     }
   };
-  issue(0);
   for (int k = 0; k < ntiles; ++k) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // tile k landed; stores of tile k-2 done
     issue(k + 1);
