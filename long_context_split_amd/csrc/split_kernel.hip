@@ -111,13 +111,12 @@ __device__ __forceinline__ float sum_x32(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// max(a, b, c) in one instruction.  Scores are finite or -inf, never NaN, so the
-// NaN-quieting copies that fmaxf would add are not needed.
-__device__ __forceinline__ float max3(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-}
+// max(a, b, c); the compiler folds the pair into one v_max3_f32.  It must stay
+// visible to the compiler: its operands come straight from MFMA accumulators,
+// and only the compiler inserts the wait states that a VALU read of an MFMA
+// result needs (the hardware does not check that dependency; an inline-asm
+// read right after the MFMA sees the register's old contents).
+__device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 
 // Neumaier compensated add of x into (sum, comp).
 __device__ __forceinline__ void comp_add(float& sum, float& comp, float x) {

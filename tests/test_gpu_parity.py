@@ -78,6 +78,16 @@ def test_q_sweep(nq):
     check_all(res, inp.numpy())
 
 
+@pytest.mark.parametrize("nq", [1, 2])
+def test_small_q_full_tiles(nq):
+    # 12000 keys in 80 splits: chunks of whole 64-key tiles with no masked key,
+    # where a score tile's row max reads the MFMA results directly.
+    _note(f"full 64-key tiles q={nq} L=12000")
+    inp = _layer([12000], nq, seed=2100 + nq)
+    res, _, _ = _run(inp)
+    check_all(res, inp.numpy())
+
+
 @pytest.mark.parametrize("ns,S", [(1, 0), (7, 0), (80, 0), (256, 0), (80, 64), (2, 3296), (80, 3296), (130, 32)])
 def test_split_variants(ns, S):
     L = 4160
@@ -245,7 +255,8 @@ def _chunk_ranges(L, ns, C, split_tokens=0):
     return out
 
 
-@pytest.mark.parametrize("lens,nq,ns", [([4096], 8, 80), ([20000], 5, 80), ([1500], 1, 40)])
+@pytest.mark.parametrize("lens,nq,ns", [([4096], 8, 80), ([20000], 5, 80), ([1500], 1, 40), ([8192], 1, 80),
+                                         ([32768], 2, 80)])
 def test_chunk_states_match_oracle_key_ranges(lens, nq, ns):
     inp = _layer(lens, nq, seed=1200 + nq)
     _note(f"split_chunks L={lens} q{nq} ns={ns}")
@@ -270,3 +281,34 @@ def test_chunk_states_match_oracle_key_ranges(lens, nq, ns):
                 m[0, i, h, j, c], l[0, i, h, j, c], o[0, i, h, j, c] = A.range_state_at(
                     *a, b=0, i=i, h=h, lo=lo, hi=hi)
     check_ws(gm, gl, gn, m, l, o)
+
+
+def test_many_sequences_of_mixed_lengths():
+    # B * NS = 480 > 256: one key chunk per split, many workgroups; lengths from
+    # the query window itself to several thousand keys, including ones that end
+    # inside a page and inside a 32-key tile.
+    lens = [8, 4160, 33, 1000, 2593, 64]
+    _note(f"batch of {len(lens)} lengths {lens} q=8")
+    inp = _layer(lens, 8, seed=3100)
+    res, _, desc = _run(inp)
+    assert dfv.chunks(desc) == 1
+    check_all(res, inp.numpy(), num_splits=80, split_tokens=0)
+
+
+@pytest.mark.parametrize("nq,layer", [(1, 0), (6, 9)])
+def test_full_size_small_q_sampled(nq, layer):
+    _note(f"full size ctx261888 q={nq} layer {layer}")
+    inp = synth.workload_layer("ctx261888_smallq_16layer", layer, num_q=nq, device="cuda")
+    res, _, _ = _run(inp)
+    d = inp.numpy()
+    a = (d["q"], d["k_cache"], d["v_cache"], d["block_table"], d["context_lens"], d["k_scale"],
+         d["v_scale"], d["softmax_scale"])
+    rows = [(0, 0), (nq - 1, 5)]
+    ref = A.reference_rows_at(*a, b=0, rows=rows)
+    for k, (i, h) in enumerate(rows):
+        check_out(res["out"][0, i, h][None], ref[k][None])
+    for (i, h, j) in [(0, 0, 0), (nq - 1, 5, 79), (0, 3, 41)]:
+        mj, lj, oj = A.split_state_at(*a, b=0, i=i, h=h, j=j)
+        check_ws(res["ws_max"][0, i, h, j][None], res["ws_sum"][0, i, h, j][None],
+                 res["ws_num"][0, i, h, j][None], np.array([mj]), np.array([lj]), oj[None])
+    assert np.all(np.isfinite(res["out"]))
