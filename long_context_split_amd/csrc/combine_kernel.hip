@@ -21,7 +21,8 @@
 // splits j = v, v+8, ... with each lane owning one dimension and all loads of a
 // batch issued before use; the eight partial sums are added in wave order
 // through LDS.  Every sum has a fixed order, so results are byte-deterministic.
-// Workspace stores are non-temporal: nothing in the launch reads them back.
+// Workspace stores are non-temporal: nothing in the launch reads them back;
+// the state loads are non-temporal too (each state is read once).
 #include "dfv_common.h"
 
 namespace dfv {
@@ -72,7 +73,7 @@ __global__ __launch_bounds__(kCombineWaves * 64) void combine_kernel(CombineArgs
       const size_t s0 = (size_t)(in ? j : 0) * C;
 #pragma unroll
       for (int c = 0; c < C; ++c) {
-        ov[b][c] = *(const float4v*)(orow + (s0 + c) * kHeadDim);
+        ov[b][c] = __builtin_nontemporal_load((const float4v*)(orow + (s0 + c) * kHeadDim));
         mv[b][c] = mrow[s0 + c];
         lv[b][c] = lrow[s0 + c];
         if (!in) mv[b][c] = kNegInf;

@@ -71,6 +71,13 @@ __device__ __forceinline__ void lds_dma16_qk(const void* base, unsigned off, LDS
                :: "v"(off), "s"(base), "s"(m0) : "memory", "m0");
 }
 
+// The same with the non-temporal hint, for the K pages (each is read once).
+__device__ __forceinline__ void lds_dma16_qk_nt(const void* base, unsigned off, LDS_AS uint8_t* dst) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)dst);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+               :: "v"(off), "s"(base), "s"(m0) : "memory", "m0");
+}
+
 __shared__ __attribute__((aligned(16))) uint8_t g_qk_k[kQkWaves][2][kQkTileBytes];
 __shared__ __attribute__((aligned(16))) uint8_t g_qk_q[kQkRB * 8][64 * 16];
 
@@ -134,12 +141,12 @@ __global__ __launch_bounds__(kQkThreads) void qk_kernel(QkArgs a) {
     const int id0 = __builtin_amdgcn_readlane(page_v, k);
     const uint8_t* p0 = a.k_cache + (size_t)id0 * kPageBytes;
 #pragma unroll
-    for (int qq = 0; qq < 4; ++qq) lds_dma16_qk(p0, lane_off[0][qq], slot + qq * 1024);
+    for (int qq = 0; qq < 4; ++qq) lds_dma16_qk_nt(p0, lane_off[0][qq], slot + qq * 1024);
     if (kTile * t + kPage < L) {
       const int id1 = __builtin_amdgcn_readlane(page_v, 32 + k);
       const uint8_t* p1 = a.k_cache + (size_t)id1 * kPageBytes;
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq) lds_dma16_qk(p1, lane_off[1][qq], slot + kPageBytes + qq * 1024);
+      for (int qq = 0; qq < 4; ++qq) lds_dma16_qk_nt(p1, lane_off[1][qq], slot + kPageBytes + qq * 1024);
     }
   };
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // page ids (and this wave's Q fragments)

@@ -137,6 +137,13 @@ __device__ __forceinline__ void lds_dma16(const void* base, unsigned off, LDS_AS
                :: "v"(off), "s"(base), "s"(m0) : "memory", "m0");
 }
 
+// The same load with the non-temporal hint: the K/V pages are read once.
+__device__ __forceinline__ void lds_dma16_nt(const void* base, unsigned off, LDS_AS uint8_t* dst) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)dst);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+               :: "v"(off), "s"(base), "s"(m0) : "memory", "m0");
+}
+
 // 4-byte direct-to-LDS load: lane l's dword lands at dst + 4*l.
 __device__ __forceinline__ void lds_dma4(const void* base, unsigned off, LDS_AS void* dst) {
   const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)dst);
@@ -282,9 +289,9 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
     const uint8_t* kp = k_cache + (size_t)page * kPageBytes;
     const uint8_t* vp = v_cache + (size_t)page * kPageBytes;
 #pragma unroll
-    for (int qq = 0; qq < 4; ++qq) lds_dma16(kp, lane_off[qq], st + qq * 1024);
+    for (int qq = 0; qq < 4; ++qq) lds_dma16_nt(kp, lane_off[qq], st + qq * 1024);
 #pragma unroll
-    for (int qq = 0; qq < 4; ++qq) lds_dma16(vp, lane_off[qq], st + kVOffset + qq * 1024);
+    for (int qq = 0; qq < 4; ++qq) lds_dma16_nt(vp, lane_off[qq], st + kVOffset + qq * 1024);
   };
   // Block-table entries come through LDS windows (one dword per lane, window
   // k = tiles 64k..64k+63, double-buffered) and then one VGPR, so no scalar
@@ -454,7 +461,7 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) lds_dma16(kvp[ks], lane_off[mb], dst + ks * kVOffset + mb * 1024);
+        for (int mb = 0; mb < 4; ++mb) lds_dma16_nt(kvp[ks], lane_off[mb], dst + ks * kVOffset + mb * 1024);
     }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
