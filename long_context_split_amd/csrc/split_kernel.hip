@@ -317,8 +317,6 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
     const int row = min(16 * rb + n, ROWS - 1);
     limit[rb] = min(L - NQ + row / kQHeads, key_end - 1);
   }
-  const int lim_min = min(L - NQ, key_end - 1);   // tiles past this hold keys some row must not see
-  auto masked_tile = [&](int t) { return key_lo + kTileKeys * t + kTileKeys - 1 > lim_min; };
 
   // Rows of this wave's V page at or past the chunk end hold unrelated bytes
   // (or nothing, for a page that was not loaded): clear their codes to +0 so
@@ -372,18 +370,16 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
       for (int rb = 0; rb < RB; ++rb)
         sacc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, qf[rb][2 * i + 1], sacc[rb], 0, 0, 0);
     }
+    // Masked keys become -inf in every tile, with selects rather than behind
+    // a uniform "tile has masked keys" branch: after such a branch the first
+    // reads of the MFMA results sit at its join, and on the branch-taken path
+    // the compiler has been seen to leave out the wait states that a VALU read
+    // of an MFMA result needs (the hardware does not check that dependency).
+    const int kb = key_lo + kTileKeys * t + 16 * wave + 4 * g;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) s[rb][r] = sacc[rb][r];
-    if (masked_tile(t)) {
-      const int kb = key_lo + kTileKeys * t + 16 * wave + 4 * g;
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (kb + r > limit[rb]) s[rb][r] = kNegInf;
-    }
+      for (int r = 0; r < 4; ++r) s[rb][r] = (kb + r > limit[rb]) ? kNegInf : sacc[rb][r];
   };
   // Running max of this lane's s - mr (cross-lane reduction only at the chunk end).
   auto lane_max = [&](const float (&s)[RB][4]) {
