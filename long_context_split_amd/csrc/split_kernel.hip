@@ -151,15 +151,6 @@ __device__ __forceinline__ void lds_dma4(const void* base, unsigned off, LDS_AS 
                :: "v"(off), "s"(base), "s"(m0) : "memory", "m0");
 }
 
-// a ^ k computed in the loop body.  The swizzled LDS addresses of a tile are
-// loop-invariant; left to itself the compiler hoists all of them out of the
-// tile loop and keeps them in registers the loop needs for operands.
-__device__ __forceinline__ unsigned xor_in_loop(unsigned a, unsigned k) {
-  unsigned r;
-  asm volatile("v_xor_b32 %0, %1, %2" : "=v"(r) : "s"(k), "v"(a));
-  return r;
-}
-
 // Wait until at most `pending` (0, 8, 16 or 24) of this wave's LDS loads are in flight.
 __device__ __forceinline__ void wait_dma(int pending) {
   if (pending >= 24) asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
