@@ -78,6 +78,27 @@ def test_q_sweep(nq):
     check_all(res, inp.numpy())
 
 
+@pytest.mark.parametrize("nq,L", [(1, 8192), (2, 32768), (3, 32768), (8, 32768)])
+def test_repeated_runs_are_byte_identical(nq, L):
+    # Every row block count with chunks of two and three 64-key tiles: a read
+    # of a value before it is ready shows up as run-to-run differences.
+    _note(f"determinism q={nq} L={L}")
+    inp = _layer([L], nq, seed=1200 + nq)
+    desc = dfv.desc_for(inp)
+    outs = []
+    for _ in range(3):
+        cb = dfv.chunk_buffers(desc)
+        for t in cb:
+            t.fill_(7.0)
+        dfv.attn_split_chunks(desc, inp.q, inp.k_cache, inp.v_cache, inp.block_table, inp.context_lens,
+                              inp.k_scale, inp.v_scale, *cb)
+        torch.cuda.synchronize()
+        outs.append([t.cpu().numpy() for t in cb])
+    for o in outs[1:]:
+        for a, b in zip(outs[0], o):
+            assert np.array_equal(a, b, equal_nan=True)
+
+
 @pytest.mark.parametrize("nq", [1, 2])
 def test_small_q_full_tiles(nq):
     # 12000 keys in 80 splits: chunks of whole 64-key tiles with no masked key,
