@@ -22,7 +22,9 @@
 //     a four-stage LDS ring fed by 16-byte direct-to-LDS loads
 //     (global_load_lds_dwordx4); the first four tiles go out as soon as the
 //     block table has arrived, and afterwards two tiles are in flight while
-//     one is scored and one is multiplied into V.  Inside a 256-byte token row
+//     one is scored and one is multiplied into V.  The page loads carry the
+//     non-temporal hint (every page is read once; 6% on this pattern).  Inside
+//     a 256-byte token row
 //     the 16-byte chunks are XOR-swizzled by the row's slot and the page's
 //     parity so operand reads are conflict free.
 //   * Eight waves, two per SIMD, split each tile by role.  For QK^T score wave
