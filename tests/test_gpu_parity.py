@@ -109,8 +109,10 @@ def test_small_q_full_tiles(nq):
     check_all(res, inp.numpy())
 
 
-@pytest.mark.parametrize("ns,S", [(1, 0), (7, 0), (80, 0), (256, 0), (80, 64), (2, 3296), (80, 3296), (130, 32)])
+@pytest.mark.parametrize("ns,S", [(1, 0), (7, 0), (80, 0), (100, 0), (256, 0), (80, 64), (2, 3296), (80, 3296),
+                                  (130, 32)])
 def test_split_variants(ns, S):
+    # Chunks per split: 4 (1, 2, 7 splits), 3 (80), 2 (100), 1 (130, 256).
     L = 4160
     if S and ns * S < L:
         pytest.skip("splits do not cover the context")
