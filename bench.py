@@ -9,10 +9,13 @@ Printed: one JSON line with the headline metric (ms per 16-layer attention;
 also its per-step median/p10/p90 and the same step replayed as a captured HIP
 graph), the roofline of the dominant kernel (split kernel: algorithmic KV
 bytes per launch / its average launch time, measured with HIP events on the
-launch stream), the split stage and the combine alone, the small-q sweep
+launch stream), the two kernels of a layer each alone (the split kernel and
+the merge+combine), the split stage and the combine from a finished
+workspace, the small-q sweep
 (q = 1..7 over the same KV), the box's page-read ceiling (a probe that streams
 exactly the layer's K and V pages in block-table order and computes nothing),
-and the CPU oracle's time on a bounded sample (rank 0, N=1 only).
+and the CPU oracle's time on a bounded sample (rank 0, N=1 only): layer 0 of
+the timed step, whose outputs are then compared with the oracle's.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--no-cpu-baseline] [--graph]
@@ -78,25 +81,39 @@ def measured_traffic(launch_bytes_alg: float):
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(workload: str, num_q: int):
-    """Time the FP64 oracle (as it stands) on one full-size layer of the workload."""
+def cpu_baseline(workload: str, d: dict, gpu: dict):
+    """Time the FP64 oracle (as it stands) on one full-size layer of the timed
+    step (host copies of layer 0's inputs), then compare that layer's outputs
+    from the timed step with the oracle's, element by element, with the
+    tolerances of the parity tests."""
     import numpy as np
-    from long_context_split_amd import synth
     from oracle import attention as A
-    inp = synth.workload_layer(workload, 0, num_q=num_q, device="cpu")
-    d = inp.numpy()
     a = (d["q"], d["k_cache"], d["v_cache"], d["block_table"], d["context_lens"], d["k_scale"],
          d["v_scale"], d["softmax_scale"])
     t0 = time.perf_counter()
-    A.attention(*a)
+    out = A.attention(*a)
     m, l, o = A.split_states(*a)
     A.combine(m, l, o)
     dt = time.perf_counter() - t0
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return dict(value=round(dt * 16 * 1000.0, 1), unit="ms per 16-layer attention (16 x one layer)",
+    base = dict(value=round(dt * 16 * 1000.0, 1), unit="ms per 16-layer attention (16 x one layer)",
                 cores=min(threads, os.cpu_count() or threads), kind="oracle",
-                sample=f"layer 0 of {workload}: unsplit FP64 attention + {A.NUM_SPLITS} split states "
-                       f"+ merge at the full context, {dt:.2f} s, scaled x16 layers")
+                sample=f"layer 0 of {workload} (the timed step's inputs): unsplit FP64 attention + "
+                       f"{A.NUM_SPLITS} split states + merge at the full context, {dt:.2f} s, scaled x16 layers")
+    # |out - ref| <= 2e-3 + 2e-3 |ref|; max within 1e-5 max(1, |m|); sum 1e-5 relative;
+    # numerator 1e-5 relative in the max norm of each (row, split); empty splits exact
+    go = gpu["out"].astype(np.float64)
+    out_excess = float(np.max(np.abs(go - out) - (2e-3 + 2e-3 * np.abs(out))))
+    full = np.isfinite(m)
+    empty_ok = bool(np.array_equal(np.isfinite(gpu["ws_max"]), full) and not gpu["ws_sum"][~full].any()
+                    and not gpu["ws_num"][~full].any())
+    dm = float(np.max(np.abs(gpu["ws_max"][full] - m[full]) / np.maximum(1.0, np.abs(m[full]))))
+    dl = float(np.max(np.abs(gpu["ws_sum"][full] - l[full]) / l[full]))
+    do = float(np.max(np.abs(gpu["ws_num"][full] - o[full]).max(axis=-1) / np.abs(o[full]).max(axis=-1)))
+    check = dict(layer=0, outputs=int(go.size), split_states=int(full.sum()),
+                 out_worst_err_minus_bound=out_excess, ws_max_rel=dm, ws_sum_rel=dl, ws_num_rel=do,
+                 ok=bool(np.all(np.isfinite(go)) and out_excess <= 0 and empty_ok and max(dm, dl, do) <= 1e-5))
+    return base, check
 
 
 def main():
@@ -142,6 +159,11 @@ def main():
             dfv.attn_split_chunks(desc, inp.q, inp.k_cache, inp.v_cache, inp.block_table,
                                   inp.context_lens, inp.k_scale, inp.v_scale, *cb)
 
+    def merge_combine_only():
+        # the second kernel of dfv_attn: key-chunk states -> workspace and FP16 output
+        for cb, ws in zip(cbufs, wss):
+            dfv.attn_combine_chunks(desc, *cb, ws.ws_max, ws.ws_sum, ws.ws_num, ws.out)
+
     def timed(fn, reps):
         """Total ms of `reps` calls, and the ms of each, from HIP events on the stream."""
         cur = torch.cuda.current_stream()
@@ -174,12 +196,22 @@ def main():
     total_ms, per_step = (graph_total, graph_steps) if args.graph else (stream_total, stream_steps)
     ms_per_step = total_ms / args.steps
     q10, q50, q90 = (float(x) for x in np.percentile(np.asarray(per_step), [10, 50, 90]))
+    # layer 0 of the timed step, kept on the host for the oracle comparison of
+    # the cpu_baseline leg (later measurements rewrite the caches' last rows)
+    checked = None
+    if not args.no_cpu_baseline:
+        checked = (layers[0].numpy(),
+                   dict(out=wss[0].out.float().cpu().numpy(), ws_max=wss[0].ws_max.cpu().numpy(),
+                        ws_sum=wss[0].ws_sum.cpu().numpy(), ws_num=wss[0].ws_num.cpu().numpy()))
 
     # dominant kernel alone (the split kernel writing key-chunk states), launched
     # on the stream; then the split stage and the combine alone as graph replays
     for _ in range(args.warmup):
         split_kernel_only()
     kernel_ms = timed(split_kernel_only, args.steps)[0] / (args.steps * len(layers))
+    for _ in range(args.warmup):
+        merge_combine_only()
+    merge_ms = timed(merge_combine_only, args.steps)[0] / (args.steps * len(layers))
     split_ms = combine_ms = None
     if not args.no_extras:
         split_ms = timed(capture(split_only).replay, args.steps)[0] / (args.steps * len(layers))
@@ -312,8 +344,13 @@ def main():
         "kv_GBps_whole_step": round(kv_bytes_layer * len(layers) / (ms_per_step * 1e-3) / 1e9, 1),
         "all_bytes_GBps_whole_step": round(all_bytes_layer * len(layers) / (ms_per_step * 1e-3) / 1e9, 1),
         "split_kernel_ms_per_launch": round(kernel_ms, 5),
+        "merge_combine_ms_per_launch": round(merge_ms, 5),
+        "per_layer_us": {"split_kernel": round(kernel_ms * 1000, 2), "merge_combine": round(merge_ms * 1000, 2),
+                         "sum_of_kernels": round((kernel_ms + merge_ms) * 1000, 2),
+                         "step_per_layer": round(ms_per_step * 1000 / len(layers), 2),
+                         "what": "the two kernels dfv_attn launches per layer, each timed alone over the 16 layers"},
         "split_stage_ms_per_call": round(split_ms, 5) if split_ms else None,
-        "combine_ms_per_call": round(combine_ms, 5) if combine_ms else None,
+        "combine_from_workspace_ms_per_call": round(combine_ms, 5) if combine_ms else None,
         "key_chunks_per_split": dfv.chunks(desc),
         "small_q_ms_per_step": small_q or None,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -342,10 +379,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         line["calibration_copy_bytes"] = 512 << 20
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(args.workload, nq)
+    if checked is not None:
+        line["cpu_baseline"], line["timed_output_check"] = cpu_baseline(args.workload, *checked)
     else:
-        line["cpu_baseline"] = None
+        line["cpu_baseline"] = line["timed_output_check"] = None
     print(json.dumps(line), flush=True)
 
 

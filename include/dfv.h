@@ -95,7 +95,9 @@ typedef enum {
  * head_dim = 256, block_size = 16, 1 <= num_q <= 8, 1 <= num_splits <= 256,
  * batch >= 1, batch * num_splits <= 2^20, split_tokens = 0 or a positive
  * multiple of 32 with num_splits * split_tokens >= max_context_len,
- * num_q <= max_context_len <= 16 * max_blocks_per_seq, softmax_scale > 0 and
+ * num_q <= max_context_len <= min(16 * max_blocks_per_seq, 2^22) (2^22 =
+ * 4194304 tokens, sixteen times the pages' 262144-token capacity, keeps every
+ * key index of the kernels inside 32-bit arithmetic), softmax_scale > 0 and
  * finite. */
 typedef struct {
   int32_t batch;              /* B                                                   */
@@ -128,6 +130,16 @@ DFV_API dfv_status dfv_attn_check(const dfv_attn_desc* desc);
  * meaningless between calls.  Calls that may overlap in time must not share a
  * scratch buffer.  Returns the descriptor's status. */
 DFV_API dfv_status dfv_attn_scratch_bytes(const dfv_attn_desc* desc, size_t* bytes);
+
+/* Every byte the split stage writes for `desc`, from one call: the workspace
+ * (ws_max and ws_sum, B*q*6*NS floats each; ws_num, B*q*6*NS*256 floats)
+ * plus the scratch that dfv_attn_scratch_bytes reports.  The workspace is an
+ * output whose layout the pages fix ([#589] Test Plan: the full FP32
+ * numerator/max/sum workspace is compared), the scratch is internal; they
+ * stay separate arguments so the workspace keeps exactly that layout and a
+ * caller can reuse one scratch buffer across layers.  Returns 0 when the
+ * descriptor is not admitted (shape-guarded admission: [#556] Purpose). */
+DFV_API size_t dfv_attn_workspace_bytes(const dfv_attn_desc* desc);
 
 /* Split stage: per-split FP32 states of every row ([#587] Implementation:
  * 80 logical splits, 32-key online updates, compensated FP32 sums, probability
@@ -167,6 +179,22 @@ DFV_API dfv_status dfv_attn_split_chunks(const dfv_attn_desc* desc, const void* 
                                  const float* k_scale, const float* v_scale,
                                  float* chunk_max, float* chunk_sum, float* chunk_num,
                                  void* stream);
+
+/* The split stage's second kernel on its own: merges the C chunk states of
+ * every (row, split) written by dfv_attn_split_chunks, in chunk order, into
+ * the workspace (ws_max, ws_sum, ws_num; the same values dfv_attn_split
+ * writes) and, when out is not NULL, forms the FP16 output from exactly the
+ * values written, as dfv_attn does ([#589] Test Result: one combine kernel
+ * follows each attention kernel).  dfv_attn_split_chunks followed by this
+ * call gives the bytes of dfv_attn.  With C = 1 the chunk states are copied
+ * into the workspace, or, when chunk_num is ws_num (and then chunk_max is
+ * ws_max and chunk_sum is ws_sum, else DFV_ERR_ARG), only read.  The chunk
+ * buffers must not overlap the workspace otherwise.
+ * Alignment: chunk_num, ws_num and out 16 bytes; others 4 bytes. */
+DFV_API dfv_status dfv_attn_combine_chunks(const dfv_attn_desc* desc, const float* chunk_max,
+                                   const float* chunk_sum, const float* chunk_num,
+                                   float* ws_max, float* ws_sum, float* ws_num, void* out,
+                                   void* stream);
 
 /* Combine stage: merges the NS split states of every row into the FP16 output
  * ([#589] Test Result: one combine kernel follows each q8 attention kernel).

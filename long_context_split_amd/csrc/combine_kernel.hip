@@ -100,13 +100,13 @@ __global__ __launch_bounds__(kCombineWaves * 64) void combine_kernel(CombineArgs
 #pragma unroll
           for (int i = 0; i < 4; ++i) oj[i] = __builtin_fmaf(ov[b][c][i], e, oj[i]);
         }
-        if (j < NS) {
-          const size_t w = (size_t)row * NS + j;
-          __builtin_nontemporal_store(oj, (float4v*)(a.ws_num + w * kHeadDim + 64 * quarter + 4 * d));
-          if (quarter == 0 && d == 0) {
-            __builtin_nontemporal_store(mj, a.ws_max + w);
-            __builtin_nontemporal_store(lj, a.ws_sum + w);
-          }
+      }
+      if ((C > 1 || a.write_ws) && j < NS) {
+        const size_t w = (size_t)row * NS + j;
+        __builtin_nontemporal_store(oj, (float4v*)(a.ws_num + w * kHeadDim + 64 * quarter + 4 * d));
+        if (quarter == 0 && d == 0) {
+          __builtin_nontemporal_store(mj, a.ws_max + w);
+          __builtin_nontemporal_store(lj, a.ws_sum + w);
         }
       }
       if (OUT) {

@@ -28,7 +28,7 @@ dfv_status check_desc(const dfv_attn_desc* d) {
   if (d->num_splits < 1 || d->num_splits > dfv::kMaxSplits) return DFV_ERR_UNSUPPORTED;
   if (d->batch < 1 || d->max_blocks_per_seq < 1) return DFV_ERR_ARG;
   if ((long long)d->batch * d->num_splits > (1LL << 20)) return DFV_ERR_ARG;
-  if (d->max_context_len < d->num_q) return DFV_ERR_ARG;
+  if (d->max_context_len < d->num_q || d->max_context_len > dfv::kMaxContext) return DFV_ERR_ARG;
   if ((long long)d->max_context_len > 16LL * d->max_blocks_per_seq) return DFV_ERR_ARG;
   if (d->split_tokens < 0 || d->split_tokens % dfv::kTile != 0) return DFV_ERR_ARG;
   if (d->split_tokens > 0 && (long long)d->split_tokens * d->num_splits < d->max_context_len)
@@ -71,6 +71,7 @@ struct ChunkStates {
 ChunkStates chunk_states(const dfv_attn_desc* d, void* scratch) {
   ChunkStates c;
   c.chunks = dfv::split_chunks(d->batch, d->num_splits);
+  if (c.chunks == 1) scratch = nullptr;   // one chunk: the split kernel writes the workspace itself
   const size_t n = dfv::scratch_floats(d->batch * d->num_q * dfv::kQHeads, d->num_splits, c.chunks);
   c.num = (float*)scratch;
   c.max = c.num ? c.num + n * kHeadDim : nullptr;
@@ -104,20 +105,24 @@ dfv_status launch_split_checked(const dfv_attn_desc* d, const void* q, const uin
   return dfv::launch_split(a, stream) == hipSuccess ? DFV_OK : DFV_ERR_LAUNCH;
 }
 
-// Merge of chunk states into the workspace (chunks > 1), and/or the combine
-// into `out` (out != NULL).  With chunks = 1 and out = NULL there is nothing
-// to do.
+// Merge of chunk states into the workspace (chunks > 1, or one chunk held in
+// buffers other than the workspace: then a copy), and/or the combine into
+// `out` (out != NULL).  With the workspace as the only states and out = NULL
+// there is nothing to do.
 dfv_status launch_combine_checked(const dfv_attn_desc* d, const ChunkStates& cs, float* wm, float* wl,
                                   float* wn, void* out, hipStream_t stream) {
-  if (cs.chunks == 1 && !out) return DFV_OK;
+  // With one chunk the states are the workspace unless the caller named other buffers.
+  const bool own = cs.chunks > 1 || (cs.num && cs.num != wn);
+  if (!own && !out) return DFV_OK;
   dfv::CombineArgs a;
   a.chunks = cs.chunks;
-  a.src_max = cs.chunks > 1 ? cs.max : wm;
-  a.src_sum = cs.chunks > 1 ? cs.sum : wl;
-  a.src_num = cs.chunks > 1 ? cs.num : wn;
+  a.src_max = own ? cs.max : wm;
+  a.src_sum = own ? cs.sum : wl;
+  a.src_num = own ? cs.num : wn;
   a.ws_max = wm;
   a.ws_sum = wl;
   a.ws_num = wn;
+  a.write_ws = own;
   a.out = (_Float16*)out;
   a.rows = d->batch * d->num_q * dfv::kQHeads;
   a.num_splits = d->num_splits;
@@ -149,6 +154,12 @@ dfv_status dfv_attn_scratch_bytes(const dfv_attn_desc* desc, size_t* bytes) {
   const dfv_status s = check_desc(desc);
   if (s == DFV_OK) *bytes = scratch_need(desc);
   return s;
+}
+
+size_t dfv_attn_workspace_bytes(const dfv_attn_desc* desc) {
+  if (check_desc(desc) != DFV_OK) return 0;
+  const size_t states = (size_t)desc->batch * desc->num_q * dfv::kQHeads * desc->num_splits;
+  return states * (2 + kHeadDim) * sizeof(float) + scratch_need(desc);
 }
 
 dfv_status dfv_attn_split(const dfv_attn_desc* desc, const void* q, const uint8_t* k_cache,
@@ -192,14 +203,31 @@ dfv_status dfv_attn_split_chunks(const dfv_attn_desc* desc, const void* q, const
                               chunk_max, chunk_sum, chunk_num, cs, (hipStream_t)stream);
 }
 
+dfv_status dfv_attn_combine_chunks(const dfv_attn_desc* desc, const float* chunk_max,
+                                   const float* chunk_sum, const float* chunk_num, float* ws_max,
+                                   float* ws_sum, float* ws_num, void* out, void* stream) {
+  dfv_status s = check_desc(desc);
+  if (s != DFV_OK) return s;
+  if (!chunk_max || !chunk_sum || !chunk_num || !ws_max || !ws_sum || !ws_num) return DFV_ERR_NULL;
+  if (!aligned(chunk_num, 16) || !aligned(ws_num, 16) || !aligned(chunk_max, 4) || !aligned(chunk_sum, 4) ||
+      !aligned(ws_max, 4) || !aligned(ws_sum, 4) || !aligned(out, 16))
+    return DFV_ERR_ALIGN;
+  ChunkStates cs{dfv::split_chunks(desc->batch, desc->num_splits), (float*)chunk_num, (float*)chunk_max,
+                 (float*)chunk_sum};
+  // One chunk per split: the chunk states are split states; they are copied into
+  // the workspace unless they already are the workspace.
+  if (cs.chunks == 1 && cs.num == ws_num && (cs.max != ws_max || cs.sum != ws_sum)) return DFV_ERR_ARG;
+  return launch_combine_checked(desc, cs, ws_max, ws_sum, ws_num, out, (hipStream_t)stream);
+}
+
 dfv_status dfv_attn_combine(const dfv_attn_desc* desc, const float* ws_max, const float* ws_sum,
                             const float* ws_num, void* out, void* stream) {
   dfv_status s = check_desc(desc);
   if (s != DFV_OK) return s;
   s = check_combine_ptrs(ws_max, ws_sum, ws_num, out);
   if (s != DFV_OK) return s;
-  ChunkStates cs{1, nullptr, nullptr, nullptr};
-  // With one chunk the workspace is only read.
+  ChunkStates cs{1, (float*)ws_num, (float*)ws_max, (float*)ws_sum};
+  // With one chunk whose states are the workspace itself, the workspace is only read.
   return launch_combine_checked(desc, cs, (float*)ws_max, (float*)ws_sum, (float*)ws_num, out,
                                 (hipStream_t)stream);
 }

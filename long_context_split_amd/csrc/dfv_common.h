@@ -18,6 +18,7 @@ constexpr int kTile = 32;                       // split boundaries fall on 32-k
 constexpr int kMaxQ = 8;
 constexpr int kMaxRows = kMaxQ * kQHeads;       // 48 query rows = three 16-row MFMA blocks
 constexpr int kMaxSplits = 256;
+constexpr int kMaxContext = 1 << 22;            // admitted bound on max_context_len (keeps key arithmetic in int)
 constexpr int kTargetCUs = 256;                 // MI355X compute units (sizes the key chunking)
 constexpr int kMaxChunks = 4;                   // key chunks per logical split, at most
 constexpr int kWaves = 4;                       // one wave per SIMD
@@ -55,10 +56,11 @@ struct CombineArgs {
   const float* src_sum;
   const float* src_num;
   int chunks;
-  // Merged workspace, written only when chunks > 1.
+  // Merged workspace, written when write_ws is set (always when chunks > 1).
   float* ws_max;
   float* ws_sum;
   float* ws_num;
+  int write_ws;
   _Float16* out;      // NULL: merge only (no output)
   int rows;           // batch * num_q * 6
   int num_splits;

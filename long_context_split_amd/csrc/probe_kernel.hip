@@ -20,11 +20,12 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "dfv_device.h"
 #include "dfv_probe.h"
 
 namespace {
 
-#define LDS_AS __attribute__((address_space(3)))
+#define LDS_AS DFV_LDS
 
 constexpr int kWavesPerWG = 8;
 constexpr int kPageBytes = 4096;
@@ -32,12 +33,6 @@ constexpr int kSlots = 2;
 constexpr int kDepth = 1;   // page pairs in flight per wave besides the one waited for
 
 __shared__ __attribute__((aligned(16))) uint8_t g_slots[kWavesPerWG][kSlots][2 * kPageBytes];
-
-__device__ __forceinline__ void lds_dma16(const void* base, unsigned off, LDS_AS uint8_t* dst) {
-  const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)dst);
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
-               :: "v"(off), "s"(base), "s"(m0) : "memory", "m0");
-}
 
 __global__ __launch_bounds__(kWavesPerWG * 64) void page_read_probe(const uint8_t* __restrict__ k,
                                                                    const uint8_t* __restrict__ v,
@@ -56,9 +51,9 @@ __global__ __launch_bounds__(kWavesPerWG * 64) void page_read_probe(const uint8_
       const size_t pg = (size_t)pages[p0 + i] * kPageBytes;
       LDS_AS uint8_t* dst = (LDS_AS uint8_t*)&g_slots[wave][i % kSlots][0];
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq) lds_dma16(k + pg, qq * 1024 + lane * 16, dst + qq * 1024);
+      for (int qq = 0; qq < 4; ++qq) dfv::lds_dma16_nt(k + pg, qq * 1024 + lane * 16, dst + qq * 1024);
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq) lds_dma16(v + pg, qq * 1024 + lane * 16, dst + kPageBytes + qq * 1024);
+      for (int qq = 0; qq < 4; ++qq) dfv::lds_dma16_nt(v + pg, qq * 1024 + lane * 16, dst + kPageBytes + qq * 1024);
     }
     if (i >= kDepth) {
       // page i - kDepth has landed once at most the pages issued after it remain

@@ -36,47 +36,17 @@
 //     as one contiguous 6q x 128-byte block, with non-temporal stores (nothing
 //     in the launch reads it back), one tile after it was computed.
 #include "dfv_qk.h"
+#include "dfv_device.h"
 
 namespace dfv {
 namespace {
 
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef _Float16 half2v __attribute__((ext_vector_type(2)));
-typedef float float4v __attribute__((ext_vector_type(4)));
-typedef unsigned uint4v __attribute__((ext_vector_type(4)));
-
-#define LDS_AS __attribute__((address_space(3)))
+#define LDS_AS DFV_LDS
 
 constexpr int kQkThreads = kQkWaves * 64;
 constexpr int kQkTileBytes = 2 * kPageBytes;   // the K pages of one 32-key tile
 constexpr int kQkRB = kMaxRows / 16;           // three 16-row blocks at most
 constexpr float kNegInfQk = -__builtin_inff();
-
-// Eight E4M3 codes (two dwords) to eight FP16 values, two codes per instruction.
-__device__ __forceinline__ half8 decode8_qk(unsigned lo, unsigned hi) {
-  const half2v a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false);
-  const half2v b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true);
-  const half2v c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false);
-  const half2v d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true);
-  return half8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-}
-
-// 16-byte direct-to-LDS load: lane l's 16 bytes (uniform base + per-lane
-// offset) land at LDS address dst + 16*l.  Inline asm, so the compiler adds no
-// blanket wait before unrelated LDS reads; the tile loop waits itself.  s_nop
-// covers the M0 write -> LDS-DMA wait state.
-__device__ __forceinline__ void lds_dma16_qk(const void* base, unsigned off, LDS_AS uint8_t* dst) {
-  const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)dst);
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :: "v"(off), "s"(base), "s"(m0) : "memory", "m0");
-}
-
-// The same with the non-temporal hint, for the K pages (each is read once).
-__device__ __forceinline__ void lds_dma16_qk_nt(const void* base, unsigned off, LDS_AS uint8_t* dst) {
-  const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)dst);
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
-               :: "v"(off), "s"(base), "s"(m0) : "memory", "m0");
-}
 
 __shared__ __attribute__((aligned(16))) uint8_t g_qk_k[kQkWaves][2][kQkTileBytes];
 __shared__ __attribute__((aligned(16))) uint8_t g_qk_q[kQkRB * 8][64 * 16];
@@ -105,7 +75,7 @@ __global__ __launch_bounds__(kQkThreads) void qk_kernel(QkArgs a) {
     const _Float16* qb = a.q + (size_t)b * ROWS * kHeadDim;
     for (int f = wave; f < RB * 8; f += kQkWaves) {
       const int row = min(16 * (f >> 3) + n, ROWS - 1);
-      lds_dma16_qk(qb, (unsigned)(row * kHeadDim * 2 + 128 * g + 16 * (f & 7)),
+      lds_dma16(qb, (unsigned)(row * kHeadDim * 2 + 128 * g + 16 * (f & 7)),
                    (LDS_AS uint8_t*)&g_qk_q[f][0]);
     }
   }
@@ -141,12 +111,12 @@ __global__ __launch_bounds__(kQkThreads) void qk_kernel(QkArgs a) {
     const int id0 = __builtin_amdgcn_readlane(page_v, k);
     const uint8_t* p0 = a.k_cache + (size_t)id0 * kPageBytes;
 #pragma unroll
-    for (int qq = 0; qq < 4; ++qq) lds_dma16_qk_nt(p0, lane_off[0][qq], slot + qq * 1024);
+    for (int qq = 0; qq < 4; ++qq) lds_dma16_nt(p0, lane_off[0][qq], slot + qq * 1024);
     if (kTile * t + kPage < L) {
       const int id1 = __builtin_amdgcn_readlane(page_v, 32 + k);
       const uint8_t* p1 = a.k_cache + (size_t)id1 * kPageBytes;
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq) lds_dma16_qk_nt(p1, lane_off[1][qq], slot + kPageBytes + qq * 1024);
+      for (int qq = 0; qq < 4; ++qq) lds_dma16_nt(p1, lane_off[1][qq], slot + kPageBytes + qq * 1024);
     }
   };
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // page ids (and this wave's Q fragments)
@@ -198,8 +168,8 @@ __global__ __launch_bounds__(kQkThreads) void qk_kernel(QkArgs a) {
       for (int j = 0; j < 4; ++j) kr[j] = *(const LDS_AS uint4v*)(krow + ((16u * (4 * g + j)) ^ swz));
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const half8 k0 = decode8_qk(kr[j][0], kr[j][1]);
-        const half8 k1 = decode8_qk(kr[j][2], kr[j][3]);
+        const half8 k0 = decode8(kr[j][0], kr[j][1]);
+        const half8 k1 = decode8(kr[j][2], kr[j][3]);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
           sacc[p][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, qf[rb][2 * j], sacc[p][rb], 0, 0, 0);

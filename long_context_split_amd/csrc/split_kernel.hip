@@ -54,19 +54,12 @@
 //     applied during decode: k_scale is folded into the score scale and v_scale
 //     into the stored numerator.
 #include "dfv_common.h"
+#include "dfv_device.h"
 
 namespace dfv {
 namespace {
 
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef _Float16 half4 __attribute__((ext_vector_type(4)));
-typedef _Float16 half2v __attribute__((ext_vector_type(2)));
-typedef float float4v __attribute__((ext_vector_type(4)));
-typedef int int2v __attribute__((ext_vector_type(2)));
-typedef unsigned uint4v __attribute__((ext_vector_type(4)));
-typedef unsigned uint2v __attribute__((ext_vector_type(2)));
-
-#define LDS_AS __attribute__((address_space(3)))
+#define LDS_AS DFV_LDS
 
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kPScale = 8.0f;              // 2^3: P * 2^3 <= 2^15 keeps FP16 hi finite
@@ -82,15 +75,6 @@ constexpr int kSplitThreads = 2 * kThreads;  // four score waves + four PV waves
 constexpr int kORowBytes = 4 * kHeadDim + 16;  // numerator row staged in LDS; the pad spreads 16 rows over all banks
 constexpr int kORowsPerStage = kTileBytes / kORowBytes;   // 31 rows of one ring stage
 static_assert(2 * kORowsPerStage >= kMaxRows, "two ring stages hold the staged numerator rows");
-
-// Eight E4M3 codes (two dwords) to eight FP16 values, two codes per instruction.
-__device__ __forceinline__ half8 decode8(unsigned lo, unsigned hi) {
-  const half2v a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false);
-  const half2v b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true);
-  const half2v c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false);
-  const half2v d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true);
-  return half8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-}
 
 // Pairwise exchange with lane ^ 16 and lane ^ 32: both lanes of a pair receive
 // the same (low-lane, high-lane) values, so symmetric reductions agree bitwise.
@@ -125,32 +109,6 @@ __device__ __forceinline__ void comp_add(float& sum, float& comp, float x) {
   const float t = sum + x;
   comp += (fabsf(sum) >= fabsf(x)) ? ((sum - t) + x) : ((x - t) + sum);
   sum = t;
-}
-
-// 16-byte direct-to-LDS load: lane l's 16 bytes (uniform base + per-lane offset)
-// land at LDS address dst + 16*l.  Issued through inline asm so the compiler does
-// not add its conservative "wait for every LDS DMA" before unrelated LDS reads;
-// the tile loop waits on vmcnt itself (vector loads complete in order, so extra
-// outstanding loads only ever make the compiler's own waits stricter).  s_nop
-// covers the M0 write -> LDS-DMA wait state.
-__device__ __forceinline__ void lds_dma16(const void* base, unsigned off, LDS_AS uint8_t* dst) {
-  const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)dst);
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :: "v"(off), "s"(base), "s"(m0) : "memory", "m0");
-}
-
-// The same load with the non-temporal hint: the K/V pages are read once.
-__device__ __forceinline__ void lds_dma16_nt(const void* base, unsigned off, LDS_AS uint8_t* dst) {
-  const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)dst);
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
-               :: "v"(off), "s"(base), "s"(m0) : "memory", "m0");
-}
-
-// 4-byte direct-to-LDS load: lane l's dword lands at dst + 4*l.
-__device__ __forceinline__ void lds_dma4(const void* base, unsigned off, LDS_AS void* dst) {
-  const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)dst);
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
-               :: "v"(off), "s"(base), "s"(m0) : "memory", "m0");
 }
 
 // Wait until at most `pending` (0, 8, 16 or 24) of this wave's LDS loads are in flight.

@@ -17,9 +17,9 @@ LIB_PATH = os.path.join(PKG, "libdfv.so")
 DFV_OK = 0
 STATUS = {0: "DFV_OK", -1: "DFV_ERR_NULL", -2: "DFV_ERR_UNSUPPORTED", -3: "DFV_ERR_ALIGN",
           -4: "DFV_ERR_ARG", -5: "DFV_ERR_LAUNCH", -7: "DFV_ERR_SCRATCH"}
-ENTRY_POINTS = ("dfv_status_string", "dfv_attn_check", "dfv_attn_scratch_bytes", "dfv_attn_chunks",
-                "dfv_attn_split_chunks", "dfv_attn_split", "dfv_attn_combine", "dfv_attn", "dfv_qk_scores",
-                "dfv_kv_append")
+ENTRY_POINTS = ("dfv_status_string", "dfv_attn_check", "dfv_attn_scratch_bytes", "dfv_attn_workspace_bytes",
+                "dfv_attn_chunks", "dfv_attn_split_chunks", "dfv_attn_combine_chunks", "dfv_attn_split",
+                "dfv_attn_combine", "dfv_attn", "dfv_qk_scores", "dfv_kv_append")
 
 
 class DfvError(RuntimeError):
@@ -54,6 +54,10 @@ def lib():
         L.dfv_attn_check.restype = ctypes.c_int
         L.dfv_attn_scratch_bytes.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(ctypes.c_size_t)]
         L.dfv_attn_scratch_bytes.restype = ctypes.c_int
+        L.dfv_attn_workspace_bytes.argtypes = [ctypes.POINTER(Desc)]
+        L.dfv_attn_workspace_bytes.restype = ctypes.c_size_t
+        L.dfv_attn_combine_chunks.argtypes = [ctypes.POINTER(Desc)] + [_P] * 7 + [_P]
+        L.dfv_attn_combine_chunks.restype = ctypes.c_int
         L.dfv_attn_chunks.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(ctypes.c_int32)]
         L.dfv_attn_chunks.restype = ctypes.c_int
         L.dfv_attn_split_chunks.argtypes = [ctypes.POINTER(Desc)] + [_P] * 10 + [_P]
@@ -87,6 +91,11 @@ def scratch_bytes(desc: Desc) -> int:
     n = ctypes.c_size_t(0)
     _raise(lib().dfv_attn_scratch_bytes(ctypes.byref(desc), ctypes.byref(n)), "dfv_attn_scratch_bytes")
     return int(n.value)
+
+
+def workspace_bytes(desc: Desc) -> int:
+    """dfv_attn_workspace_bytes: workspace (max, sum, numerator) plus scratch bytes; 0 if not admitted."""
+    return int(lib().dfv_attn_workspace_bytes(ctypes.byref(desc)))
 
 
 def chunks(desc: Desc) -> int:
@@ -159,6 +168,14 @@ def chunk_buffers(desc: Desc, device="cuda"):
     return (torch.empty(*rows, dtype=torch.float32, device=device),
             torch.empty(*rows, dtype=torch.float32, device=device),
             torch.empty(*rows, desc.head_dim, dtype=torch.float32, device=device))
+
+
+def attn_combine_chunks(desc: Desc, chunk_max, chunk_sum, chunk_num, ws_max, ws_sum, ws_num, out,
+                        stream=None):
+    """dfv_attn_combine_chunks: chunk states -> workspace (and the FP16 output unless out is None)."""
+    st = lib().dfv_attn_combine_chunks(ctypes.byref(desc), _ptr(chunk_max), _ptr(chunk_sum), _ptr(chunk_num),
+                                       _ptr(ws_max), _ptr(ws_sum), _ptr(ws_num), _ptr(out), _stream(stream))
+    _raise(st, "dfv_attn_combine_chunks")
 
 
 def attn_combine(desc: Desc, ws_max, ws_sum, ws_num, out, stream=None):

@@ -147,6 +147,54 @@ def make_layer(context_lens: Sequence[int], num_q: int, *, seed_base: int, layer
         meta=dict(seed_base=seed_base, layer=layer, key_mix=key_mix, num_q=num_q))
 
 
+def make_periodic_layer(context_len: int, num_q: int, period: int, *, seed_base: int, device="cpu",
+                        scales=(0.125, 0.125)) -> LayerInputs:
+    """One sequence whose key and value rows repeat with `period` tokens.
+
+    Token t holds row t mod period of a K pattern and of a V pattern (each drawn
+    and quantized as in :func:`make_layer`); pages are placed on a seeded random
+    permutation with the same poison as there.  A long context then needs only
+    the patterns to describe it (``meta["k_pattern"]``, ``meta["v_pattern"]``:
+    uint8 [period, 256]).
+    """
+    device = torch.device(device)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed_base * 1_000_003 + period)
+    L = int(context_len)
+    if L < num_q:
+        raise ValueError("the context must hold the q query tokens")
+    k_scale = float(torch.tensor(float(scales[0]), dtype=torch.float32))
+    v_scale = float(torch.tensor(float(scales[1]), dtype=torch.float32))
+    kp = quantize_e4m3(torch.randn(period, HEAD_DIM, generator=gen, device=device), k_scale)
+    vp = quantize_e4m3(torch.randn(period, HEAD_DIM, generator=gen, device=device), v_scale)
+    npg = -(-L // BLOCK_SIZE)
+    num_blocks = npg + SPARE_PAGES
+    perm = torch.randperm(num_blocks, generator=gen, device=device)
+    q = torch.randn(1, num_q, HQ, HEAD_DIM, generator=gen, device=device, dtype=torch.float32).to(torch.float16)
+    k_cache = torch.full((num_blocks, BLOCK_SIZE, HKV, HEAD_DIM), POISON_CODE, dtype=torch.uint8, device=device)
+    v_cache = torch.full_like(k_cache, POISON_CODE)
+    phys = perm[:npg]
+    step = 1 << 16                                   # pages per write, bounds the temporaries
+    for p0 in range(0, npg, step):
+        p1 = min(npg, p0 + step)
+        t = torch.arange(p0 * BLOCK_SIZE, p1 * BLOCK_SIZE, device=device)
+        kr = kp[t % period]
+        vr = vp[t % period]
+        past = t >= L
+        kr[past] = POISON_CODE
+        vr[past] = POISON_CODE
+        k_cache[phys[p0:p1], :, 0, :] = kr.view(p1 - p0, BLOCK_SIZE, HEAD_DIM)
+        v_cache[phys[p0:p1], :, 0, :] = vr.view(p1 - p0, BLOCK_SIZE, HEAD_DIM)
+    block_table = phys.to(torch.int32).view(1, npg).clone()
+    return LayerInputs(
+        q=q, k_cache=k_cache, v_cache=v_cache, block_table=block_table,
+        context_lens=torch.tensor([L], dtype=torch.int32, device=device),
+        k_scale=torch.tensor([k_scale], dtype=torch.float32, device=device),
+        v_scale=torch.tensor([v_scale], dtype=torch.float32, device=device),
+        softmax_scale=1.0 / (HEAD_DIM ** 0.5),
+        meta=dict(seed_base=seed_base, period=period, num_q=num_q, k_pattern=kp, v_pattern=vp))
+
+
 # Named workloads: the pages' q8 / Hq6 / Hkv1 / D256 verification attention at the
 # context lengths they measure (up to the 261888-token capacity boundary).
 WORKLOADS = {

@@ -185,3 +185,43 @@ def test_kv_append_refuses_bad_arguments_before_launch(L):
     assert call(vc=P((1 << 21) + 4)) == -3
     assert call(sl=P(12288 + 4)) == -3
     assert call(n=0) == 0          # nothing to write: returns before any launch
+
+
+def test_workspace_bytes_cover_workspace_and_scratch(L):
+    # q8 x 6 heads x 80 splits: (max, sum, 256-float numerator) per state, plus
+    # the three key-chunk states per split staged in scratch
+    d = _good()
+    ws = 48 * 80 * (2 + 256) * 4
+    assert dfv.workspace_bytes(d) == ws + dfv.scratch_bytes(d) == ws + 48 * 80 * 3 * 258 * 4
+    # one chunk per split (4 sequences x 80 splits): the workspace only
+    d4 = _good(batch=4)
+    assert dfv.workspace_bytes(d4) == 4 * 48 * 80 * 258 * 4 and dfv.scratch_bytes(d4) == 0
+    assert dfv.workspace_bytes(_good(num_q=9)) == 0      # not admitted
+    assert L.dfv_attn_workspace_bytes(None) == 0
+
+
+def test_context_length_bound(L):
+    big = 1 << 22
+    assert dfv.check(_good(max_context_len=big, max_blocks=big // 16)) == 0
+    assert dfv.check(_good(max_context_len=big + 1, max_blocks=big // 16 + 1)) == -4
+
+
+def test_combine_chunks_refuses_bad_arguments_before_launch(L):
+    d = _good()
+    P = ctypes.c_void_p
+    ok = [P(4096 * (i + 1)) for i in range(7)]      # chunk max/sum/num, ws max/sum/num, out
+    assert L.dfv_attn_combine_chunks(ctypes.byref(_good(num_q=9)), *ok, None) == -2
+    for k in range(6):
+        args = list(ok)
+        args[k] = None
+        assert L.dfv_attn_combine_chunks(ctypes.byref(d), *args, None) == -1
+    args = list(ok)
+    args[2] = P(4096 * 3 + 4)                          # chunk_num misaligned
+    assert L.dfv_attn_combine_chunks(ctypes.byref(d), *args, None) == -3
+    args = list(ok)
+    args[6] = P(4096 * 7 + 8)                          # out misaligned
+    assert L.dfv_attn_combine_chunks(ctypes.byref(d), *args, None) == -3
+    # one chunk per split with the numerator aliasing the workspace but the max not
+    d4 = _good(batch=4)
+    args = [P(4096), P(8192), P(1 << 20), P(1 << 21), P(1 << 22), P(1 << 20), P(1 << 23)]
+    assert L.dfv_attn_combine_chunks(ctypes.byref(d4), *args, None) == -4

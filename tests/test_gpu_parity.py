@@ -3,8 +3,8 @@
 Inputs come from the seeded synthetic generator; the oracle receives host copies
 of the very same arrays.  Sizes are small enough for the oracle to finish in
 seconds while spanning many 32-key tiles, several workgroups per split and a
-ragged tail; the full-size checks at the end sample outputs the oracle can
-compute one at a time.
+ragged tail.  The workloads' full sizes are compared element by element in
+test_gpu_full_size.py.
 """
 import sys
 
@@ -241,28 +241,6 @@ def test_bad_descriptor_is_refused_without_launch():
     assert bool((ws.out == 7.0).all())
 
 
-# ------------------------------------------------------------------ full sizes, sampled
-
-@pytest.mark.parametrize("name,layer", [("ctx32768_16layer", 3), ("ctx131072_peaky_16layer", 11),
-                                        ("ctx261888_16layer", 0), ("ctx261888_16layer", 15)])
-def test_full_size_sampled(name, layer):
-    _note(f"full size {name} layer {layer}")
-    inp = synth.workload_layer(name, layer, device="cuda")
-    res, _, _ = _run(inp)
-    d = inp.numpy()
-    a = (d["q"], d["k_cache"], d["v_cache"], d["block_table"], d["context_lens"], d["k_scale"],
-         d["v_scale"], d["softmax_scale"])
-    rows = [(0, 0), (3, 4), (7, 5)]
-    ref = A.reference_rows_at(*a, b=0, rows=rows)
-    for k, (i, h) in enumerate(rows):
-        check_out(res["out"][0, i, h][None], ref[k][None])
-    for (i, h, j) in [(0, 0, 0), (7, 5, 79), (4, 2, 40), (7, 0, 78), (1, 3, 13)]:
-        mj, lj, oj = A.split_state_at(*a, b=0, i=i, h=h, j=j)
-        check_ws(res["ws_max"][0, i, h, j][None], res["ws_sum"][0, i, h, j][None],
-                 res["ws_num"][0, i, h, j][None], np.array([mj]), np.array([lj]), oj[None])
-    assert np.all(np.isfinite(res["out"]))
-
-
 def _chunk_ranges(L, ns, C, split_tokens=0):
     """Key range [lo, hi) of every (split j, chunk c), restating the layout that
     dfv_attn_split_chunks documents: tiles of 32 keys cut per split, then into
@@ -316,22 +294,3 @@ def test_many_sequences_of_mixed_lengths():
     res, _, desc = _run(inp)
     assert dfv.chunks(desc) == 1
     check_all(res, inp.numpy(), num_splits=80, split_tokens=0)
-
-
-@pytest.mark.parametrize("nq,layer", [(1, 0), (6, 9)])
-def test_full_size_small_q_sampled(nq, layer):
-    _note(f"full size ctx261888 q={nq} layer {layer}")
-    inp = synth.workload_layer("ctx261888_smallq_16layer", layer, num_q=nq, device="cuda")
-    res, _, _ = _run(inp)
-    d = inp.numpy()
-    a = (d["q"], d["k_cache"], d["v_cache"], d["block_table"], d["context_lens"], d["k_scale"],
-         d["v_scale"], d["softmax_scale"])
-    rows = [(0, 0), (nq - 1, 5)]
-    ref = A.reference_rows_at(*a, b=0, rows=rows)
-    for k, (i, h) in enumerate(rows):
-        check_out(res["out"][0, i, h][None], ref[k][None])
-    for (i, h, j) in [(0, 0, 0), (nq - 1, 5, 79), (0, 3, 41)]:
-        mj, lj, oj = A.split_state_at(*a, b=0, i=i, h=h, j=j)
-        check_ws(res["ws_max"][0, i, h, j][None], res["ws_sum"][0, i, h, j][None],
-                 res["ws_num"][0, i, h, j][None], np.array([mj]), np.array([lj]), oj[None])
-    assert np.all(np.isfinite(res["out"]))

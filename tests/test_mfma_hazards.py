@@ -17,7 +17,30 @@ import pytest
 
 from long_context_split_amd import build as B
 
-MIN_WAIT_STATES = 8   # below anything the compiler leaves on a straight-line path in these kernels
+# Wait states needed between an XDL MFMA that writes a VGPR and the first
+# VALU, LDS, memory or MFMA source-A/B read of it.  The CDNA3 ISA's MAI
+# dependency table gives passes + 3 for this case (2, 4, 8, 16 passes -> 5, 7,
+# 11, 19); gfx950 needs one more once an MFMA has more than two passes.  The
+# compiler's own hazard model agrees on the one MFMA these kernels use: it
+# places s_nop 7 (8 wait states) between v_mfma_f32_16x16x32_f16, a 4-pass XDL
+# operation on gfx950, and a VALU reader of its result.  An MFMA missing from
+# the table fails the scan, so the table grows with the kernels.
+XDL_PASSES = {
+    "v_mfma_f32_16x16x32_f16": 4,
+    "v_mfma_f32_16x16x32_bf16": 4,
+    "v_mfma_f32_32x32x16_f16": 8,
+    "v_mfma_f32_32x32x16_bf16": 8,
+}
+
+
+def required_wait_states(op):
+    if op not in XDL_PASSES:
+        raise KeyError(f"no pass count for {op}: add it to XDL_PASSES")
+    p = XDL_PASSES[op]
+    return p + 3 + (1 if p > 2 else 0)
+
+
+MIN_WAIT_STATES = None   # None: each MFMA's own requirement from XDL_PASSES
 _REG = re.compile(r"([va])\[(\d+):(\d+)\]|([va])(\d+)")
 
 
@@ -47,12 +70,13 @@ def _parse(text):
 
 def early_reads(text, min_ws=MIN_WAIT_STATES):
     """(mfma index, reader text, wait states) for every read of an MFMA result
-    reached with fewer than min_ws wait states along some path."""
+    reached with fewer wait states than that MFMA needs (min_ws, when given,
+    replaces the per-MFMA requirement) along some path."""
     ins, labels = _parse(text)
     found = []
 
-    def walk(j, dst, ws, depth, seen, src):
-        while j < len(ins) and ws < min_ws:
+    def walk(j, dst, ws, depth, seen, src, need):
+        while j < len(ins) and ws < need:
             t = ins[j]
             op = t[0]
             if op == "s_nop":
@@ -65,7 +89,7 @@ def early_reads(text, min_ws=MIN_WAIT_STATES):
                 tgt = t[1]
                 if tgt in labels and depth < 4 and (tgt, ws) not in seen:
                     seen.add((tgt, ws))
-                    walk(labels[tgt], dst, ws + 1, depth + 1, seen, src)
+                    walk(labels[tgt], dst, ws + 1, depth + 1, seen, src, need)
                 if op == "s_branch":
                     return
                 ws += 1
@@ -90,7 +114,9 @@ def early_reads(text, min_ws=MIN_WAIT_STATES):
 
     for i, t in enumerate(ins):
         if t[0].startswith("v_mfma"):
-            walk(i + 1, _regs(t[1]), 0, 0, set(), i)
+            need = required_wait_states(t[0]) if min_ws is None else min_ws
+
+            walk(i + 1, _regs(t[1]), 0, 0, set(), i, need)
     return found
 
 
@@ -140,3 +166,30 @@ def test_scan_accepts_enough_wait_states_and_accumulation():
     s_endpgm
 """
     assert early_reads(ok) == []
+
+
+def test_requirement_follows_the_pass_count():
+    # an 8-pass MFMA read after ten wait states is still too early (it needs 12);
+    # a 4-pass one is too early after seven and fine after eight
+    planted = """
+    v_mfma_f32_32x32x16_f16 v[0:15], v[16:19], v[20:23], v[0:15]
+    s_nop 7
+    s_nop 1
+    v_add_f32_e32 v30, v1, v31
+    s_endpgm
+"""
+    bad = early_reads(planted)
+    assert len(bad) == 1 and bad[0][2] == 10
+    four = """
+    v_mfma_f32_16x16x32_f16 v[4:7], v[8:11], a[0:3], v[4:7]
+    s_nop 6
+    v_add_f32_e32 v30, v5, v31
+    s_endpgm
+"""
+    assert [b[2] for b in early_reads(four)] == [7]
+    assert early_reads(four.replace("s_nop 6", "s_nop 7")) == []
+
+
+def test_unknown_mfma_is_refused():
+    with pytest.raises(KeyError):
+        early_reads("    v_mfma_f32_4x4x4_16b_f16 v[0:3], v[4:5], v[6:7], v[0:3]\n    s_endpgm\n")
