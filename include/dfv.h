@@ -213,6 +213,22 @@ DFV_API dfv_status dfv_attn(const dfv_attn_desc* desc, const void* q, const uint
                     float* ws_max, float* ws_sum, float* ws_num, void* scratch,
                     size_t scratch_bytes, void* out, void* stream);
 
+/* dfv_attn for callers that cannot allocate (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same arguments
+ * and results as dfv_attn without the scratch pair.  The key-chunk states go
+ * to a static device array of 16 MiB inside the library (each GPU holds its
+ * own copy until the process ends), which covers every admitted descriptor
+ * (at most 12,681,216 bytes); a descriptor needing more would return
+ * DFV_ERR_SCRATCH.  The call allocates nothing; on its first use on a device
+ * it looks up that device's array address (DFV_ERR_LAUNCH if the runtime
+ * refuses).  Every call on one GPU shares that GPU's array, so calls that may
+ * overlap in time on one GPU (other streams, other threads) race: serialize
+ * them.  The array needs no initialisation between calls. */
+DFV_API dfv_status dfv_attn_noalloc(const dfv_attn_desc* desc, const void* q, const uint8_t* k_cache,
+                            const uint8_t* v_cache, const int32_t* block_table,
+                            const int32_t* context_lens, const float* k_scale, const float* v_scale,
+                            float* ws_max, float* ws_sum, float* ws_num, void* out, void* stream);
+
 /* QK stage on its own ([#589] Purpose: the QK producer the pages time by
  * itself, without softmax, PV or the split merge; [#589] Test Plan: checked
  * score by score and guard tile by guard tile before timing).  Computes

@@ -23,7 +23,8 @@ PROBE_PATH = os.path.join(PKG, PROBE_NAME)
 PROBE_SOURCES = ["probe_kernel.hip"]
 ARCH = "gfx950"
 
-SOURCES = ["split_kernel.hip", "combine_kernel.hip", "qk_kernel.hip", "kv_append_kernel.hip", "dfv_api.cpp"]
+SOURCES = ["split_kernel.hip", "combine_kernel.hip", "qk_kernel.hip", "kv_append_kernel.hip", "dfv_api.cpp",
+           "noalloc.hip"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -19,7 +19,7 @@ STATUS = {0: "DFV_OK", -1: "DFV_ERR_NULL", -2: "DFV_ERR_UNSUPPORTED", -3: "DFV_E
           -4: "DFV_ERR_ARG", -5: "DFV_ERR_LAUNCH", -7: "DFV_ERR_SCRATCH"}
 ENTRY_POINTS = ("dfv_status_string", "dfv_attn_check", "dfv_attn_scratch_bytes", "dfv_attn_workspace_bytes",
                 "dfv_attn_chunks", "dfv_attn_split_chunks", "dfv_attn_combine_chunks", "dfv_attn_split",
-                "dfv_attn_combine", "dfv_attn", "dfv_qk_scores", "dfv_kv_append")
+                "dfv_attn_combine", "dfv_attn", "dfv_attn_noalloc", "dfv_qk_scores", "dfv_kv_append")
 
 
 class DfvError(RuntimeError):
@@ -68,6 +68,8 @@ def lib():
         L.dfv_attn_combine.restype = ctypes.c_int
         L.dfv_attn.argtypes = [ctypes.POINTER(Desc)] + [_P] * 10 + [_P, ctypes.c_size_t, _P, _P]
         L.dfv_attn.restype = ctypes.c_int
+        L.dfv_attn_noalloc.argtypes = [ctypes.POINTER(Desc)] + [_P] * 10 + [_P, _P]
+        L.dfv_attn_noalloc.restype = ctypes.c_int
         L.dfv_qk_scores.argtypes = [ctypes.POINTER(Desc)] + [_P] * 6 + [ctypes.c_int64, _P]
         L.dfv_qk_scores.restype = ctypes.c_int
         L.dfv_kv_append.argtypes = [_P, _P, _P, ctypes.c_int32, _P, _P, _P, _P, ctypes.c_int64, _P]
@@ -192,6 +194,15 @@ def attn(desc: Desc, q, k_cache, v_cache, block_table, context_lens, k_scale, v_
                         0 if scratch is None else scratch.numel() * scratch.element_size(),
                         _ptr(out), _stream(stream))
     _raise(st, "dfv_attn")
+
+
+def attn_noalloc(desc: Desc, q, k_cache, v_cache, block_table, context_lens, k_scale, v_scale,
+                 ws_max, ws_sum, ws_num, out, stream=None):
+    """dfv_attn_noalloc: dfv_attn with the library's static scratch (allocates nothing)."""
+    st = lib().dfv_attn_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                                _ptr(context_lens), _ptr(k_scale), _ptr(v_scale), _ptr(ws_max), _ptr(ws_sum),
+                                _ptr(ws_num), _ptr(out), _stream(stream))
+    _raise(st, "dfv_attn_noalloc")
 
 
 def qk_tiles(desc: Desc) -> int:

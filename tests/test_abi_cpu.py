@@ -225,3 +225,11 @@ def test_combine_chunks_refuses_bad_arguments_before_launch(L):
     d4 = _good(batch=4)
     args = [P(4096), P(8192), P(1 << 20), P(1 << 21), P(1 << 22), P(1 << 20), P(1 << 23)]
     assert L.dfv_attn_combine_chunks(ctypes.byref(d4), *args, None) == -4
+
+
+def test_noalloc_refuses_a_bad_descriptor_on_the_host(L):
+    # the descriptor is checked before the device array is looked up
+    P = ctypes.c_void_p
+    ok = [P(4096 * (i + 1)) for i in range(12)]
+    assert L.dfv_attn_noalloc(ctypes.byref(_good(num_q=9)), *ok, None) == -2
+    assert L.dfv_attn_noalloc(None, *ok, None) == -1
