@@ -20,9 +20,10 @@
 //     of a split in chunk order, so results are deterministic.
 //   * A workgroup walks its chunk in 64-key tiles, four 16-token pages, through
 //     a four-stage LDS ring fed by 16-byte direct-to-LDS loads
-//     (global_load_lds_dwordx4); the first four tiles go out as soon as the
-//     block table has arrived, and afterwards two tiles are in flight while
-//     one is scored and one is multiplied into V.  The page loads carry the
+//     (global_load_lds_dwordx4); the first tile goes out alone as soon as the
+//     block table has arrived, the next three once it has landed, and
+//     afterwards two tiles are in flight while one is scored and one is
+//     multiplied into V.  The page loads carry the
 //     non-temporal hint (every page is read once; 6% on this pattern).  Inside
 //     a 256-byte token row
 //     the 16-byte chunks are XOR-swizzled by the row's slot and the page's
@@ -453,18 +454,22 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
 
   // ------------------------------------------------------------------ prologue
   // The PV waves own the DMA stream: PV wave w fetches the block-table windows
-  // of page w (0 and 1) and, as soon as those land, puts page w of the first
-  // kStages tiles in flight (the ring is empty, so every stage is free); it
-  // later waits for each tile before the barrier that hands the tile to the
-  // score waves.  Meanwhile the score waves stage Q, in MFMA B-operand order,
-  // in the P buffers, which nothing else uses before P(0) is published.
+  // of page w (0 and 1) and, as soon as those land, puts page w of tile 0 in
+  // flight alone, so that it lands as early as the start allows (every
+  // workgroup issues at once, and a wave is held at each load until the memory
+  // system takes it); tiles 1..kStages-1 follow once tile 0 is in, while the
+  // score waves compute its scores.  A wave waits for each tile before the
+  // barrier that hands the tile to the score waves.  Meanwhile the score waves
+  // stage Q, in MFMA B-operand order, in the P buffers, which nothing else
+  // uses before P(0) is published.
   // Fragment f = rb*8 + m, lane (n, g) holds Q[row 16rb+n][64g + 8m + 0..7];
   // rows past 6q repeat the last real row.
   LDS_AS uint8_t* const qstage = (LDS_AS uint8_t*)&g_p[0][0];
   static_assert(sizeof(g_p) >= kMaxRB * 8 * 1024, "Q staging fits in the P buffers");
   // PV waves: windows 0 and 1 (unless the speculative ones hold the same
-  // pages), then tiles 0..kStages-1.
-  auto start_stream = [&](bool spec_ok) {
+  // pages), then tiles 0..last (the first start: tile 0 alone; a restart:
+  // all kStages tiles).
+  auto start_stream = [&](bool spec_ok, int last) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (!spec_ok) {
       if (nu > 0) load_window(0);
@@ -473,11 +478,12 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
     }
     pg = g_pages[0][wave][lane];
 #pragma unroll
-    for (int u = 0; u < kStages; ++u) issue_tile(u, pg);
+    for (int u = 0; u < kStages; ++u)
+      if (u <= last) issue_tile(u, pg);
   };
   if (!scorer) {
-    start_stream(spec_lo == page_lo && spec_end == page_end && spec_nu == nu);
-    wait_dma(pending_after(0, kStages - 1));   // tile 0 (the score waves read it after the barrier)
+    start_stream(spec_lo == page_lo && spec_end == page_end && spec_nu == nu, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // tile 0, the only one in flight
   } else {
     const _Float16* qb = q + (size_t)b * ROWS * kHeadDim;
     for (int f = wave; f < RB * 8; f += kWaves) {
@@ -612,6 +618,8 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
     // its barrier): they win issue ties on their SIMD (about 1% per launch).
     __builtin_amdgcn_s_setprio(1);
     if (nu > 0) {
+#pragma unroll
+      for (int u = 1; u < kStages; ++u) issue_tile(u, pg);   // while the score waves work on tile 0
       __syncthreads();   // first-tile max exchange
       wait_dma(pending_after(1, kStages - 2));
       __syncthreads();   // P(0) published; tile 1 landed
@@ -646,7 +654,7 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) o[mb][rb] = float4v{0.f, 0.f, 0.f, 0.f};
-      start_stream(false);
+      start_stream(false, kStages - 1);
       wait_dma(pending_after(0, kStages - 1));
       __syncthreads();   // restart: tile 0 landed
       wait_dma(pending_after(1, kStages - 2));
