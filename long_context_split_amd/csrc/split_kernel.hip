@@ -105,11 +105,23 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // read right after the MFMA sees the register's old contents).
 __device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 
-// Neumaier compensated add of x into (sum, comp).
+// Kahan compensated add of x into (sum, comp), comp holding minus the low part
+// lost so far: every term is a probability (x >= 0), so the sum only grows
+// and Kahan's bound (about 2u of the sum) holds without Neumaier's branch.
 __device__ __forceinline__ void comp_add(float& sum, float& comp, float x) {
-  const float t = sum + x;
-  comp += (fabsf(sum) >= fabsf(x)) ? ((sum - t) + x) : ((x - t) + sum);
+  const float y = x - comp;
+  const float t = sum + y;
+  comp = (t - sum) - y;
   sum = t;
+}
+
+// FP16 of p - hi, where hi is an FP16 value: one v_fma_mixlo_f16 (hi read as
+// FP16, p as FP32, the difference exact in FP32 and rounded once to FP16).
+// Neither operand is an MFMA result.
+__device__ __forceinline__ _Float16 residual_f16(_Float16 hi, float p) {
+  float out;
+  asm("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(out) : "v"(hi), "v"(p));
+  return __builtin_bit_cast(half2v, out)[0];
 }
 
 // Wait until at most `pending` (0, 8, 16 or 24) of this wave's LDS loads are in flight.
@@ -262,7 +274,9 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
   };
 
   // Causal bound of each of this lane's rows (rows past 6q act as the last
-  // real row), also cut at the chunk end.
+  // real row), also cut at the chunk end; mask_from is the first key that some
+  // row must not see, so tiles below it need no mask.
+  const int mask_from = min(L - NQ + 1, key_end);
   int limit[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
@@ -270,17 +284,21 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
     limit[rb] = min(L - NQ + row / kQHeads, key_end - 1);
   }
 
-  // Rows of this wave's V page at or past the chunk end hold unrelated bytes
-  // (or nothing, for a page that was not loaded): clear their codes to +0 so
-  // that P = 0 times V never turns into 0 * NaN.  Only the chunk's last tile.
+  // Rows of this wave's K and V pages at or past the chunk end hold unrelated
+  // bytes (or nothing, for a page that was not loaded): clear their codes to +0
+  // so that neither a masked score (-inf plus the products) nor P = 0 times V
+  // turns into NaN.  Only the chunk's last tile.
   auto clear_tail = [&](int t) {
     const int r0 = max(0, key_end - kPage * (page_lo + 4 * t + wave));
     if (r0 >= kPage) return;
-    LDS_AS uint8_t* vp = stage_of(t) + kVOffset + wave * kPageBytes;
+    LDS_AS uint8_t* kp = stage_of(t) + wave * kPageBytes;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int idx = e * 64 + lane;   // 16-byte chunk idx of the page, row idx / 16
-      if ((idx >> 4) >= r0) *(LDS_AS uint4v*)(vp + idx * 16) = uint4v{0u, 0u, 0u, 0u};
+      if ((idx >> 4) >= r0) {
+        *(LDS_AS uint4v*)(kp + idx * 16) = uint4v{0u, 0u, 0u, 0u};
+        *(LDS_AS uint4v*)(kp + kVOffset + idx * 16) = uint4v{0u, 0u, 0u, 0u};
+      }
     }
   };
 
@@ -302,11 +320,23 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
 
   // S^T - mr = K_w * Q^T - mr for this wave's page of tile t (the products
   // accumulate onto -mr); lane holds keys key_lo + 64t + 16w + 4g + r of row
-  // 16rb + n.  Masked keys get -inf.
+  // 16rb + n.  Masked keys start at -inf instead, which the (finite) products
+  // leave at -inf; only tiles that reach mask_from choose per key.  The
+  // choice is made before the MFMAs, so no branch separates an MFMA from the
+  // first reader of its result (the hardware does not check that dependency,
+  // and at such a join the compiler has been seen to leave out the wait states).
   auto qk = [&](int t, float (&s)[RB][4]) {
     float4v sacc[RB];
+    if (key_lo + kTileKeys * (t + 1) > mask_from) {
+      const int kb = key_lo + kTileKeys * t + 16 * wave + 4 * g;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) sacc[rb] = float4v{-mr[rb], -mr[rb], -mr[rb], -mr[rb]};
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sacc[rb][r] = (kb + r > limit[rb]) ? kNegInf : -mr[rb];
+    } else {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) sacc[rb] = float4v{-mr[rb], -mr[rb], -mr[rb], -mr[rb]};
+    }
     const LDS_AS uint8_t* krow = stage_of(t) + wave * kPageBytes + n * 256;
     uint4v kr[4];   // all four reads in flight at once: one LDS latency per tile
 #pragma unroll
@@ -322,16 +352,10 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
       for (int rb = 0; rb < RB; ++rb)
         sacc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, qf[rb][2 * i + 1], sacc[rb], 0, 0, 0);
     }
-    // Masked keys become -inf in every tile, with selects rather than behind
-    // a uniform "tile has masked keys" branch: after such a branch the first
-    // reads of the MFMA results sit at its join, and on the branch-taken path
-    // the compiler has been seen to leave out the wait states that a VALU read
-    // of an MFMA result needs (the hardware does not check that dependency).
-    const int kb = key_lo + kTileKeys * t + 16 * wave + 4 * g;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) s[rb][r] = (kb + r > limit[rb]) ? kNegInf : sacc[rb][r];
+      for (int r = 0; r < 4; ++r) s[rb][r] = sacc[rb][r];
   };
   // Running max of this lane's s - mr (cross-lane reduction only at the chunk end).
   auto lane_max = [&](const float (&s)[RB][4]) {
@@ -355,7 +379,7 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
       const half4 hi = half4{h01[0], h01[1], h23[0], h23[1]};
       half4 lo;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) lo[r] = (_Float16)__builtin_fmaf((float)hi[r], -1.0f, p8[r]);
+      for (int r = 0; r < 4; ++r) lo[r] = residual_f16(hi[r], p8[r]);
       comp_add(l_sum[rb], l_cmp[rb], (p8[0] + p8[1]) + (p8[2] + p8[3]));
       const int slot = ((wave >> 1) * RB + rb) * 2;
       *(LDS_AS half4*)(pw + slot * kPSlot) = hi;
@@ -557,7 +581,7 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
       for (int rb = 0; rb < RB; ++rb) {
         ovf |= m_lane[rb] * c2 > kRestartLog2;   // false while -inf
         const float mx = mr[rb] + max_x32(max_x16(m_lane[rb]));   // -inf stays -inf
-        const float l = sum_x32(sum_x16(l_sum[rb])) + sum_x32(sum_x16(l_cmp[rb]));
+        const float l = sum_x32(sum_x16(l_sum[rb])) - sum_x32(sum_x16(l_cmp[rb]));
         if (g == 0) {
           g_meta[0][wave][16 * rb + n] = mx;
           g_meta[1][wave][16 * rb + n] = l;
