@@ -37,8 +37,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0          # MI355X published HBM3E bandwidth
 V100_16LAYER_MS = 12.983        # the pages' 16-layer q8 attention on V100 (context only)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "split_kernel_traffic.json")
-SPLIT_SRCS = [os.path.join(ROOT, "long_context_split_amd", "csrc", "split_kernel.hip"),
-              os.path.join(ROOT, "long_context_split_amd", "csrc", "dfv_common.h")]
+SPLIT_SRCS = [os.path.join(ROOT, "long_context_split_amd", "csrc", n)
+              for n in ("split_kernel.hip", "dfv_common.h", "dfv_device.h")]
 
 
 def parse():
@@ -59,7 +59,7 @@ def parse():
 
 
 def src_hash() -> str:
-    """Hash of everything that shapes the split kernel's binary (source, shared header, flags)."""
+    """Hash of everything that shapes the split kernel's binary (source, shared headers, flags)."""
     from long_context_split_amd import build as B
     h = hashlib.sha256()
     for p in SPLIT_SRCS:
