@@ -25,9 +25,9 @@
 //     afterwards two tiles are in flight while one is scored and one is
 //     multiplied into V.  The page loads carry the
 //     non-temporal hint (every page is read once; 6% on this pattern).  Inside
-//     a 256-byte token row
-//     the 16-byte chunks are XOR-swizzled by the row's slot and the page's
-//     parity so operand reads are conflict free.
+//     a 256-byte token row the 16-byte chunks are XOR-swizzled by the row's
+//     slot, and the K, V and P operand orders are chosen so that the LDS
+//     serves every operand read without a bank conflict.
 //   * Eight waves, two per SIMD, split each tile by role.  For QK^T score wave
 //     w takes page w: S^T = K_w * Q^T on v_mfma_f32_16x16x32_f16 for all 6q rows
 //     (up to three 16-row blocks, Q held in registers), so every K byte is
@@ -133,7 +133,8 @@ __device__ __forceinline__ void wait_dma(int pending) {
 }
 
 __shared__ __attribute__((aligned(16))) uint8_t g_ring[kStages * kTileBytes];
-// P operands, double-buffered by tile parity: [ks][rb][hi|lo][lane][8 halves].
+// P operands, double-buffered by tile parity: [ks][rb][hi|lo][page parity][lane][4 halves],
+// as the score waves hold them (each wave writes 512 contiguous bytes per operand).
 __shared__ __attribute__((aligned(16))) uint8_t g_p[2][2 * kMaxRB * 2 * kPSlot];
 __shared__ float g_meta[3][kWaves][kMaxRows];   // per score wave: row max, row sum, reference
 __shared__ int g_flag[kWaves];                  // a wave's rows outgrew m_ref somewhere in the chunk
@@ -235,15 +236,12 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
 
   // ------------------------------------------------------------------ score waves
   // DMA lane offsets: load qq of a page fills LDS row r = 4qq + lane/16, chunk
-  // position lane%16, with global chunk (lane%16) ^ r ^ x of that row, where
-  // x = 4 * (page slot & 1): the two pages that one 32-key PV step reads
-  // together then use different banks for the same row.
-  const unsigned xpage = 4u * (unsigned)(wave & 1);
+  // position lane%16, with global chunk (lane%16) ^ r of that row.
   unsigned lane_off[4];
 #pragma unroll
   for (int qq = 0; qq < 4; ++qq) {
     const unsigned r = 4 * qq + (lane >> 4);
-    lane_off[qq] = r * 256u + 16u * ((unsigned)(lane & 15) ^ r ^ xpage);
+    lane_off[qq] = r * 256u + 16u * ((unsigned)(lane & 15) ^ r);
   }
   // Wave w's page of tile u is page_lo + 4u + w; pages past the chunk are skipped.
   auto tile_valid = [&](int u) { return u < nu && page_lo + 4 * u + wave < page_end; };
@@ -316,7 +314,7 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
     l_sum[rb] = 0.f;
     l_cmp[rb] = 0.f;
   }
-  const unsigned kswz = 16u * ((unsigned)n ^ xpage);   // K row n, chunk c at n*256 + 16*(c ^ n ^ x)
+  const unsigned kswz = 16u * (unsigned)n;   // K row n, chunk c at n*256 + 16*(c ^ n)
 
   // S^T - mr = K_w * Q^T - mr for this wave's page of tile t (the products
   // accumulate onto -mr); lane holds keys key_lo + 64t + 16w + 4g + r of row
@@ -338,9 +336,13 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
       for (int rb = 0; rb < RB; ++rb) sacc[rb] = float4v{-mr[rb], -mr[rb], -mr[rb], -mr[rb]};
     }
     const LDS_AS uint8_t* krow = stage_of(t) + wave * kPageBytes + n * 256;
+    // Read i of lane (n, g) is 16-byte chunk g + 4i of its row: the four lane
+    // groups of one read take four neighbouring chunks, which the LDS serves
+    // without bank conflicts (chunks 4g + i, the other natural order, cost a
+    // second pass on gfx950).
     uint4v kr[4];   // all four reads in flight at once: one LDS latency per tile
 #pragma unroll
-    for (int i = 0; i < 4; ++i) kr[i] = *(const LDS_AS uint4v*)(krow + ((16u * (4 * g + i)) ^ kswz));
+    for (int i = 0; i < 4; ++i) kr[i] = *(const LDS_AS uint4v*)(krow + ((16u * (g + 4 * i)) ^ kswz));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const half8 k0 = decode8(kr[i][0], kr[i][1]);
@@ -366,9 +368,9 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
   // exact remainder, rounded); compensated row sums.  s - mr comes straight
   // from the accumulation, so keys near the max keep full relative precision
   // even when |m_ref * c2| is large.  Published for every PV wave: operand
-  // (ks, rb, hi|lo), lane (n, g), halves 4(w%2)..+3, ks = w/2.
+  // (ks, rb, hi|lo) with ks = w/2, this lane's 8 bytes at 512 (w%2) + 8 lane.
   auto publish_p = [&](int t, const float (&s)[RB][4]) {
-    LDS_AS uint8_t* pw = (LDS_AS uint8_t*)g_p[t & 1] + lane * 16 + 8 * (wave & 1);
+    LDS_AS uint8_t* pw = (LDS_AS uint8_t*)g_p[t & 1] + 512 * (wave & 1) + 8 * lane;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       float p8[4];
@@ -382,8 +384,10 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
       for (int r = 0; r < 4; ++r) lo[r] = residual_f16(hi[r], p8[r]);
       comp_add(l_sum[rb], l_cmp[rb], (p8[0] + p8[1]) + (p8[2] + p8[3]));
       const int slot = ((wave >> 1) * RB + rb) * 2;
-      *(LDS_AS half4*)(pw + slot * kPSlot) = hi;
-      *(LDS_AS half4*)(pw + (slot + 1) * kPSlot) = lo;
+      // volatile: two separate ds_write_b64 (the compiler would pair them into
+      // one ds_write2st64_b64, which the LDS serves at half the rate)
+      *(volatile LDS_AS half4*)(pw + slot * kPSlot) = hi;
+      *(volatile LDS_AS half4*)(pw + (slot + 1) * kPSlot) = lo;
     }
   };
   // Scores of tile t up to (not including) publishing: tail, QK.  The PV waves
@@ -399,19 +403,22 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) o[mb][rb] = float4v{0.f, 0.f, 0.f, 0.f};
-  // V operand addresses (ds_read_b64_tr_b8): lane (n, g) reads row (page j/4,
-  // slot 4g + j%4), j = n/2, bytes 8(n%2)..+7 of 16-byte chunk mb; after the
-  // transpose it holds 8 keys of dimension 16mb + n, MFMA K-index 8g + k being
-  // key 4g + k of page 0 (k < 4) or key 4g + k - 4 of page 1.
+  // V operand addresses (ds_read_b64_tr_b8): lane (n, g) reads row (page g/2,
+  // slot 8(g%2) + (j ^ 4(g%2))), j = n/2, bytes 8(n%2)..+7 of 16-byte chunk
+  // mb; after the transpose it holds 8 keys of dimension 16mb + n, MFMA
+  // K-index 8g + k being key 8(g%2) + (k ^ 4(g%2)) of page g/2.  Each half
+  // wave reads all 16 rows of one page, which spreads its 32 reads over every
+  // bank.  The P operand follows the same key order: for even g, halves 0-3
+  // and 4-7 are the 8 bytes that score lanes (n, 0) and (n, 1) of page g/2
+  // wrote; for odd g, those of lanes (n, 3) and (n, 2).  Read in that order
+  // (as two 8-byte reads), every half wave again covers all banks.
   unsigned voff[4];
   {
-    const int vj = n >> 1;
-    const int vslot = 4 * g + (vj & 3);
-    const unsigned vx = 4u * (unsigned)(vj >> 2);   // x of page 2ks + j/4
+    const int vslot = 8 * (g & 1) + ((n >> 1) ^ (4 * (g & 1)));
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
-      voff[mb] = kVOffset + (vj >> 2) * kPageBytes + vslot * 256 + 8 * (n & 1) +
-                 ((16u * (4 * wave + mb)) ^ (16u * ((unsigned)vslot ^ vx)));
+      voff[mb] = kVOffset + (g >> 1) * kPageBytes + vslot * 256 + 8 * (n & 1) +
+                 ((16u * (4 * wave + mb)) ^ (16u * (unsigned)vslot));
   }
   // PV of tile t: 64 keys as two 32-key MFMA steps (pages 2ks, 2ks+1), for
   // this wave's four 16-dimension blocks; hi products of every row block first,
@@ -424,7 +431,8 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
   // 0.4 us longer).
   auto pv = [&](int t, int tn) {
     const unsigned sbase = (unsigned)(uintptr_t)stage_of(t);
-    const LDS_AS uint8_t* pr = (const LDS_AS uint8_t*)g_p[t & 1] + lane * 16;
+    const LDS_AS uint8_t* pr1 = (const LDS_AS uint8_t*)g_p[t & 1] + 512 * (g >> 1) + 384 * (g & 1) + 8 * n;
+    const LDS_AS uint8_t* pr2 = (const LDS_AS uint8_t*)g_p[t & 1] + 512 * (g >> 1) + 128 * ((g & 1) + 1) + 8 * n;
     const bool dma = tn >= 0 && tile_valid(tn);
     const int page = dma ? __builtin_amdgcn_readlane(pg, tn & 63) : 0;
     const uint8_t* kvp[2] = {k_cache + (size_t)page * kPageBytes, v_cache + (size_t)page * kPageBytes};
@@ -440,8 +448,13 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
       half8 phi[RB], plo[RB];
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        phi[rb] = *(const LDS_AS half8*)(pr + ((ks * RB + rb) * 2) * kPSlot);
-        plo[rb] = *(const LDS_AS half8*)(pr + ((ks * RB + rb) * 2 + 1) * kPSlot);
+        // volatile: four separate ds_read_b64, not ds_read2st64_b64 pairs
+        // (those take twice the LDS cycles)
+        const int shi = ((ks * RB + rb) * 2) * kPSlot, slo = shi + kPSlot;
+        const half4 h0 = *(volatile const LDS_AS half4*)(pr1 + shi), h1 = *(volatile const LDS_AS half4*)(pr2 + shi);
+        const half4 l0 = *(volatile const LDS_AS half4*)(pr1 + slo), l1 = *(volatile const LDS_AS half4*)(pr2 + slo);
+        phi[rb] = half8{h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+        plo[rb] = half8{l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
       }
       int2v vr[4];
 #pragma unroll
@@ -486,8 +499,9 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
   // barrier that hands the tile to the score waves.  Meanwhile the score waves
   // stage Q, in MFMA B-operand order, in the P buffers, which nothing else
   // uses before P(0) is published.
-  // Fragment f = rb*8 + m, lane (n, g) holds Q[row 16rb+n][64g + 8m + 0..7];
-  // rows past 6q repeat the last real row.
+  // Fragment f = rb*8 + m, lane (n, g) holds Q[row 16rb+n][64(m/2) + 16g +
+  // 8(m%2) + 0..7] (the dimensions of K read m/2); rows past 6q repeat the
+  // last real row.
   LDS_AS uint8_t* const qstage = (LDS_AS uint8_t*)&g_p[0][0];
   static_assert(sizeof(g_p) >= kMaxRB * 8 * 1024, "Q staging fits in the P buffers");
   // PV waves: windows 0 and 1 (unless the speculative ones hold the same
@@ -512,7 +526,8 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
     const _Float16* qb = q + (size_t)b * ROWS * kHeadDim;
     for (int f = wave; f < RB * 8; f += kWaves) {
       const int row = min(16 * (f >> 3) + n, ROWS - 1);
-      lds_dma16(qb, (unsigned)(row * kHeadDim * 2 + 128 * g + 16 * (f & 7)), qstage + f * 1024);
+      const int m = f & 7;
+      lds_dma16(qb, (unsigned)(row * kHeadDim * 2 + 128 * (m >> 1) + 32 * g + 16 * (m & 1)), qstage + f * 1024);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
