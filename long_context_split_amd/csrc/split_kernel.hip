@@ -115,13 +115,15 @@ __device__ __forceinline__ void comp_add(float& sum, float& comp, float x) {
   sum = t;
 }
 
-// FP16 of p - hi, where hi is an FP16 value: one v_fma_mixlo_f16 (hi read as
-// FP16, p as FP32, the difference exact in FP32 and rounded once to FP16).
-// Neither operand is an MFMA result.
-__device__ __forceinline__ _Float16 residual_f16(_Float16 hi, float p) {
-  float out;
-  asm("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(out) : "v"(hi), "v"(p));
-  return __builtin_bit_cast(half2v, out)[0];
+// FP16 of pa - hi.lo and pb - hi.hi, packed, where hi holds two FP16 values:
+// v_fma_mixlo_f16 and v_fma_mixhi_f16 (each difference exact in FP32 and
+// rounded once to FP16; the second instruction fills the high half and keeps
+// the low one).  No operand is an MFMA result.
+__device__ __forceinline__ unsigned residual_pair(unsigned hi, float pa, float pb) {
+  unsigned out;
+  asm("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(out) : "v"(hi), "v"(pa));
+  asm("v_fma_mixhi_f16 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "+v"(out) : "v"(hi), "v"(pb));
+  return out;
 }
 
 // Wait until at most `pending` (0, 8, 16 or 24) of this wave's LDS loads are in flight.
@@ -376,18 +378,16 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
       float p8[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) p8[r] = fast_exp2(__builtin_fmaf(s[rb][r], c2, kPScaleLog2));
-      const half2v h01 = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(p8[0], p8[1]));
-      const half2v h23 = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(p8[2], p8[3]));
-      const half4 hi = half4{h01[0], h01[1], h23[0], h23[1]};
-      half4 lo;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) lo[r] = residual_f16(hi[r], p8[r]);
+      const unsigned h01 = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(p8[0], p8[1]));
+      const unsigned h23 = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(p8[2], p8[3]));
+      const uint2v hi = uint2v{h01, h23};
+      const uint2v lo = uint2v{residual_pair(h01, p8[0], p8[1]), residual_pair(h23, p8[2], p8[3])};
       comp_add(l_sum[rb], l_cmp[rb], (p8[0] + p8[1]) + (p8[2] + p8[3]));
       const int slot = ((wave >> 1) * RB + rb) * 2;
       // volatile: two separate ds_write_b64 (the compiler would pair them into
       // one ds_write2st64_b64, which the LDS serves at half the rate)
-      *(volatile LDS_AS half4*)(pw + slot * kPSlot) = hi;
-      *(volatile LDS_AS half4*)(pw + (slot + 1) * kPSlot) = lo;
+      *(volatile LDS_AS uint2v*)(pw + slot * kPSlot) = hi;
+      *(volatile LDS_AS uint2v*)(pw + (slot + 1) * kPSlot) = lo;
     }
   };
   // Scores of tile t up to (not including) publishing: tail, QK.  The PV waves
