@@ -21,9 +21,9 @@
 //   * A workgroup walks its chunk in 64-key tiles, four 16-token pages, through
 //     a four-stage LDS ring fed by 16-byte direct-to-LDS loads
 //     (global_load_lds_dwordx4); the first tile goes out alone as soon as the
-//     block table has arrived, the next three once it has landed, and
-//     afterwards two tiles are in flight while one is scored and one is
-//     multiplied into V.  The page loads carry the
+//     block table has arrived, the next two once it has landed and the fourth
+//     with the first loop iteration; afterwards two tiles are in flight while
+//     one is scored and one is multiplied into V.  The page loads carry the
 //     non-temporal hint (every page is read once; 6% on this pattern).  Inside
 //     a 256-byte token row the 16-byte chunks are XOR-swizzled by the row's
 //     slot, and the K, V and P operand orders are chosen so that the LDS
@@ -494,8 +494,10 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
   // of page w (0 and 1) and, as soon as those land, puts page w of tile 0 in
   // flight alone, so that it lands as early as the start allows (every
   // workgroup issues at once, and a wave is held at each load until the memory
-  // system takes it); tiles 1..kStages-1 follow once tile 0 is in, while the
-  // score waves compute its scores.  A wave waits for each tile before the
+  // system takes it); tiles 1 and 2 follow once tile 0 is in, while the score
+  // waves compute its scores, and tile 3 goes out in the first loop iteration
+  // like every later tile (the less the start issues, the sooner the loop
+  // begins: 0.3-0.8 us against issuing tiles 1-3 here).  A wave waits for each tile before the
   // barrier that hands the tile to the score waves.  Meanwhile the score waves
   // stage Q, in MFMA B-operand order, in the P buffers, which nothing else
   // uses before P(0) is published.
@@ -506,7 +508,7 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
   static_assert(sizeof(g_p) >= kMaxRB * 8 * 1024, "Q staging fits in the P buffers");
   // PV waves: windows 0 and 1 (unless the speculative ones hold the same
   // pages), then tiles 0..last (the first start: tile 0 alone; a restart:
-  // all kStages tiles).
+  // tiles 0-2).
   auto start_stream = [&](bool spec_ok, int last) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (!spec_ok) {
@@ -658,18 +660,19 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
     __builtin_amdgcn_s_setprio(1);
     if (nu > 0) {
 #pragma unroll
-      for (int u = 1; u < kStages; ++u) issue_tile(u, pg);   // while the score waves work on tile 0
+      for (int u = 1; u < kStages - 1; ++u) issue_tile(u, pg);   // while the score waves work on tile 0
       __syncthreads();   // first-tile max exchange
-      wait_dma(pending_after(1, kStages - 2));
+      wait_dma(pending_after(1, kStages - 3));
       __syncthreads();   // P(0) published; tile 1 landed
     }
     for (;;) {
       for (int u = 0; u < nu; ++u) {
         // Every wave is past the barrier that ended tile u-1: its stage is free
-        // (tiles 0..kStages-1 went out before the loop).
+        // (tiles 0..kStages-2 went out before the loop; tile kStages-1 goes
+        // out now, in iteration 0).
         const int tn = u + kStages - 1;
         int tdma = -1;
-        if (u > 0 && tn < nu) {
+        if (tn < nu) {
           if ((tn & 63) == 0) {
             pg = g_pages[(tn >> 6) & 1][wave][lane];
             if (tn + 64 < nu) load_window((tn >> 6) + 1);
@@ -693,10 +696,10 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) o[mb][rb] = float4v{0.f, 0.f, 0.f, 0.f};
-      start_stream(false, kStages - 1);
-      wait_dma(pending_after(0, kStages - 1));
+      start_stream(false, kStages - 2);
+      wait_dma(pending_after(0, kStages - 2));
       __syncthreads();   // restart: tile 0 landed
-      wait_dma(pending_after(1, kStages - 2));
+      wait_dma(pending_after(1, kStages - 3));
       __syncthreads();   // P(0) published; tile 1 landed
     }
   }
