@@ -443,8 +443,12 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) lds_dma16_nt(kvp[ks], lane_off[mb], dst + ks * kVOffset + mb * 1024);
     }
+    // A tile whose pages 2 and 3 lie past the chunk (the last tile of a chunk
+    // of an odd number of 32-key tiles) needs only the first 32-key step.
+    const int nks = (page_lo + 4 * t + 2 >= page_end) ? 1 : 2;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
+      if (ks >= nks) break;
       half8 phi[RB], plo[RB];
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
