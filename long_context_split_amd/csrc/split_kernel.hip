@@ -527,7 +527,12 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
   };
   if (!scorer) {
     start_stream(spec_lo == page_lo && spec_end == page_end && spec_nu == nu, 0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // tile 0, the only one in flight
+    // Tile 0's K is all the first scores need: when the tile has no keys past
+    // the chunk end (nothing for the score waves to clear in its V), the V
+    // half may still be in flight at the barrier; the wait for tile 1 before
+    // the loop covers it.
+    if (key_lo + kTileKeys <= key_end) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   } else {
     const _Float16* qb = q + (size_t)b * ROWS * kHeadDim;
     for (int f = wave; f < RB * 8; f += kWaves) {
