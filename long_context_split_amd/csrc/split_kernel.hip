@@ -424,11 +424,12 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
   // this wave's four 16-dimension blocks; hi products of every row block first,
   // then lo, so dependent MFMAs on one accumulator are RB instructions apart.
   //
-  // When tn >= 0 the eight 1 KB loads of this wave's page of tile tn (K, then
-  // V) go out first, before the operand reads: the earlier they leave, the
-  // longer they have before the barrier that needs them (issued after the
-  // products instead, a launch takes 1.6 us longer; interleaved between them,
-  // 0.4 us longer).
+  // When tn >= 0 this wave's page of tile tn goes out in two halves: its
+  // four K loads before the operand reads (the score waves need tile tn one
+  // iteration before the PV waves do), its four V loads after the products.
+  // A wave is held at each load issue until the memory system takes it; with
+  // the V half after the products that hold overlaps the wave's MFMAs still
+  // in the pipe (all eight first: the step about 1% slower).
   auto pv = [&](int t, int tn) {
     const unsigned sbase = (unsigned)(uintptr_t)stage_of(t);
     const LDS_AS uint8_t* pr1 = (const LDS_AS uint8_t*)g_p[t & 1] + 512 * (g >> 1) + 384 * (g & 1) + 8 * n;
@@ -439,9 +440,7 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
     LDS_AS uint8_t* dst = stage_of(dma ? tn : 0) + wave * kPageBytes;
     if (dma) {
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb) lds_dma16_nt(kvp[ks], lane_off[mb], dst + ks * kVOffset + mb * 1024);
+      for (int mb = 0; mb < 4; ++mb) lds_dma16_nt(kvp[0], lane_off[mb], dst + mb * 1024);
     }
     // A tile whose pages 2 and 3 lie past the chunk (the last tile of a chunk
     // of an odd number of 32-key tiles) needs only the first 32-key step.
@@ -475,6 +474,10 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
         for (int rb = 0; rb < RB; ++rb)
           o[mb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, plo[rb], o[mb][rb], 0, 0, 0);
       }
+    }
+    if (dma) {
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) lds_dma16_nt(kvp[1], lane_off[mb], dst + kVOffset + mb * 1024);
     }
   };
 
