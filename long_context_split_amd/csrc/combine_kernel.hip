@@ -16,11 +16,12 @@
 // the same bytes as a merge followed by a combine of the workspace.
 //
 // The work is small (NS * C KB per row) and latency-bound, so it is spread
-// wide: one workgroup per (row, quarter of the 256 dimensions), eight waves.
+// wide: one workgroup per (row, quarter of the 256 dimensions), ten waves.
 // Every wave reduces M over all states itself (no barrier), then wave v takes
-// splits j = v, v+8, ... with each lane owning one dimension and all loads of a
-// batch issued before use; the eight partial sums are added in wave order
-// through LDS.  Every sum has a fixed order, so results are byte-deterministic.
+// the groups of four splits g = v, v+10, ... (two per load batch, so the 20
+// groups of an 80-split row are one batch) with each lane owning four
+// dimensions of one split and all loads of a batch issued before use; the ten
+// partial sums are added in wave order through LDS.  Every sum has a fixed order, so results are byte-deterministic.
 // Workspace stores are non-temporal: nothing in the launch reads them back;
 // the state loads are non-temporal too (each state is read once).
 #include "dfv_common.h"
@@ -29,8 +30,8 @@ namespace dfv {
 namespace {
 
 constexpr float kNegInf = -__builtin_inff();
-constexpr int kCombineWaves = 8;
-constexpr int kGroupsPerBatch = 3;   // 4-split groups per wave per load batch
+constexpr int kCombineWaves = 10;
+constexpr int kGroupsPerBatch = 2;   // 4-split groups per wave per load batch
 
 typedef float float4v __attribute__((ext_vector_type(4)));
 

@@ -24,10 +24,12 @@
 //     its tiles arrive in one vector load (lane j: page j / 32 of tile j % 32)
 //     and are then read with v_readlane, so no memory latency sits between
 //     one tile and the next tile's DMA.
-//   * Each tile's two 4 KiB K pages land in the wave's own LDS slot by 16-byte
-//     direct-to-LDS loads (global_load_lds_dwordx4), one tile ahead of the
-//     products; inside a 256-byte token row the 16-byte chunks are XOR-swizzled
-//     by row and page parity so that the operand reads fall on distinct banks.
+//   * Each tile's two 4 KiB K pages land in one of the wave's two LDS slots by
+//     16-byte direct-to-LDS loads (global_load_lds_dwordx4); a slot is read
+//     into registers as soon as its tile lands and refilled at once, so two
+//     tiles are in flight per wave while the products run; inside a 256-byte
+//     token row the 16-byte chunks are XOR-swizzled by row and page parity so
+//     that the operand reads fall on distinct banks.
 //   * S^T = K Q^T on v_mfma_f32_16x16x32_f16 with Q (staged once per workgroup
 //     through LDS) in registers; E4M3 is decoded with v_cvt_scalef32_pk_f16_fp8
 //     (exact in FP16), the per-tensor scale folded into c.
@@ -92,7 +94,6 @@ __global__ __launch_bounds__(kQkThreads) void qk_kernel(QkArgs a) {
   // At most kQkWindow by the launch geometry; the bound keeps every page-id
   // read inside the window whatever the lengths.
   const int ntiles = min(t0 < Tb ? (Tb - t0 + W - 1) / W : 0, kQkWindow);
-  const float c = a.softmax_scale * a.k_scale[0];
 
   // DMA lane offsets: load qq of page p fills LDS row r = 4qq + lane/16, chunk
   // position lane%16, with global chunk (lane%16) ^ r ^ 4p of that row.
@@ -104,6 +105,12 @@ __global__ __launch_bounds__(kQkThreads) void qk_kernel(QkArgs a) {
       const unsigned r = 4 * qq + (lane >> 4);
       lane_off[p][qq] = r * 256u + 16u * ((unsigned)(lane & 15) ^ r ^ (4u * p));
     }
+  // Number of 16-byte loads issue(k) puts out: 4 per page, the second page
+  // only when it starts inside the context; 0 past the wave's tiles.
+  auto nops = [&](int k) -> int {
+    if (k >= ntiles) return 0;
+    return (kTile * (t0 + k * W) + kPage < L) ? 8 : 4;
+  };
   auto issue = [&](int k) {
     if (k >= ntiles) return;
     const int t = t0 + k * W;
@@ -119,8 +126,12 @@ __global__ __launch_bounds__(kQkThreads) void qk_kernel(QkArgs a) {
       for (int qq = 0; qq < 4; ++qq) lds_dma16_nt(p1, lane_off[1][qq], slot + kPageBytes + qq * 1024);
     }
   };
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // page ids (and this wave's Q fragments)
-  issue(0);                                           // the first tile goes out before the barrier
+  // Page ids, the length, the scale and this wave's Q fragments have landed;
+  // c passes through the wait so that no later wait is placed for its load.
+  float c = a.softmax_scale * a.k_scale[0];
+  asm volatile("s_waitcnt vmcnt(0)" : "+v"(c) :: "memory");
+  issue(0);                                           // two tiles go out before the barrier
+  issue(1);
   __syncthreads();                                    // every wave's Q fragments staged
   half8 qf[RB][8];
 #pragma unroll
@@ -134,10 +145,13 @@ __global__ __launch_bounds__(kQkThreads) void qk_kernel(QkArgs a) {
   for (int rb = 0; rb < RB; ++rb) limit[rb] = L - NQ + min(16 * rb + n, ROWS - 1) / kQHeads;
   float* const out_b = a.scores + (size_t)b * a.tiles_per_seq * ROWS * kTile;
 
-  // A tile's scores are stored one iteration later, after the wait for the
-  // next tile: on this GPU loads and stores share one counter and may complete
-  // out of order, so every wait is a full one, and a store issued just before
-  // it would make the wave wait for the store's round trip too.
+  // Two tiles in flight per wave: tile k's slot is read into registers as
+  // soon as it lands and refilled with tile k + 2 before the products.  The
+  // wait for tile k lets the loads of tile k + 1 stay outstanding: loads
+  // complete in issue order, so at most nops(k + 1) operations outstanding
+  // means tile k has landed, whatever the stores issued in between (they may
+  // complete in any order, and are counted as still to wait for).  A tile's
+  // scores are stored one iteration later, after the refill.
   float4v res[2][RB];
   int res_t = -1;
   auto store_res = [&]() {
@@ -151,25 +165,32 @@ __global__ __launch_bounds__(kQkThreads) void qk_kernel(QkArgs a) {
     }
   };
   for (int k = 0; k < ntiles; ++k) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // tile k landed; stores of tile k-2 done
-    issue(k + 1);
-    if (res_t >= 0) store_res();
+    const int after = nops(k + 1);
+    if (after == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else if (after == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     const int t = t0 + k * W;
     const LDS_AS uint8_t* ks = (const LDS_AS uint8_t*)&g_qk_k[wave][k & 1][0] + n * 256;
+    uint4v kr[2][4];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const LDS_AS uint8_t* krow = ks + p * kPageBytes;
+      const unsigned swz = 16u * ((unsigned)n ^ (4u * p));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) kr[p][j] = *(const volatile LDS_AS uint4v*)(krow + ((16u * (4 * g + j)) ^ swz));
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the slot is read before its refill
+    issue(k + 2);
+    if (res_t >= 0) store_res();
     float4v sacc[2][RB];
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) sacc[p][rb] = float4v{0.f, 0.f, 0.f, 0.f};
-      const LDS_AS uint8_t* krow = ks + p * kPageBytes;
-      const unsigned swz = 16u * ((unsigned)n ^ (4u * p));
-      uint4v kr[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) kr[j] = *(const LDS_AS uint4v*)(krow + ((16u * (4 * g + j)) ^ swz));
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const half8 k0 = decode8(kr[j][0], kr[j][1]);
-        const half8 k1 = decode8(kr[j][2], kr[j][3]);
+        const half8 k0 = decode8(kr[p][j][0], kr[p][j][1]);
+        const half8 k1 = decode8(kr[p][j][2], kr[p][j][3]);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
           sacc[p][rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, qf[rb][2 * j], sacc[p][rb], 0, 0, 0);
