@@ -28,6 +28,7 @@ import dataclasses
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -59,12 +60,18 @@ def parse():
 
 
 def src_hash() -> str:
-    """Hash of everything that shapes the split kernel's binary (source, shared headers, flags)."""
+    """Hash of everything that shapes the split kernel's binary: its source and the
+    shared headers with comments and blank lines removed (a comment edit leaves the
+    code object unchanged), and the hipcc flags."""
     from long_context_split_amd import build as B
     h = hashlib.sha256()
     for p in SPLIT_SRCS:
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p, "r") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        code = "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+        h.update(code.encode())
     h.update(" ".join(B.HIPCC_FLAGS).encode())
     return h.hexdigest()[:16]
 

@@ -668,7 +668,7 @@ void split_kernel(const _Float16* __restrict__ q, const uint8_t* __restrict__ k_
     }
   } else {
     // The PV waves carry the tile loop's critical path (the score waves wait at
-    // its barrier): they win issue ties on their SIMD (about 1% per launch).
+    // its barrier): they win issue ties on their SIMD (about 3% per launch).
     __builtin_amdgcn_s_setprio(1);
     if (nu > 0) {
 #pragma unroll
